@@ -1,0 +1,126 @@
+"""Seeded synthetic inputs for the attention path.
+
+This module is shared by the tests, the smoke check and the benchmark, and it
+holds none of the attention arithmetic: it draws the N(0, 1) tensors and casts
+them to the storage formats the library takes.  Both the oracle and the HIP
+path consume exactly what it returns.
+
+Recipe (the same for every workload): numpy ``default_rng(seed)`` (PCG64)
+draws float32 standard normals for Q, K, V and then dO, in that order, each of
+shape [B, H, N, d] with d innermost.  The pages' own examples use N(0, 1)
+inputs (torch.randn in "FlashAttention-1: eliminating IO", sections 10.2.3 and
+10.2.4; np.random.randn with seed 42 in the V1/V2/V3 explainer's Python demo).
+
+Storage formats:
+* fp32 -- the draws as they are.
+* bf16 -- round-to-nearest-even of each float32 (torch's cast), kept as raw
+  uint16 bit patterns so nothing downstream depends on a torch dtype.
+* fp8  -- OCP float8 e4m3fn with one scale per tensor, s = amax|X| / 448, and
+  codes = round-to-nearest-even(X / s) saturated to +-448.  The explainer says
+  only that FP8 inputs are paired with scaling factors (V3 section); the
+  per-tensor amax form is the plainest reading.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "fp32" | "bf16" | "fp8"
+    causal: bool
+    backward: bool      # does the workload include the backward pass
+    scale: float
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+
+def _w(name, B, H, N, d, dtype, causal, backward):
+    return Workload(name, B, H, N, d, dtype, causal, backward, 1.0 / math.sqrt(d))
+
+
+# The five workloads: shapes, formats, mask and passes.
+WORKLOADS = {
+    "fp32_fwdbwd_b1h1n128d64": _w("fp32_fwdbwd_b1h1n128d64", 1, 1, 128, 64, "fp32", False, True),
+    "bf16_fwd_b4h16n2048d64": _w("bf16_fwd_b4h16n2048d64", 4, 16, 2048, 64, "bf16", False, False),
+    "bf16_causal_fwd_b2h32n8192d128": _w("bf16_causal_fwd_b2h32n8192d128", 2, 32, 8192, 128,
+                                          "bf16", True, False),
+    "bf16_causal_fwdbwd_b2h16n4096d128": _w("bf16_causal_fwdbwd_b2h16n4096d128", 2, 16, 4096,
+                                             128, "bf16", True, True),
+    "fp8_fwd_b1h32n16384d128": _w("fp8_fwd_b1h32n16384d128", 1, 32, 16384, 128, "fp8", False,
+                                  False),
+}
+
+
+def draw_f32(shape, seed: int = 42, count: int = 4):
+    """Draw `count` float32 N(0,1) tensors of `shape` in the order Q, K, V, dO."""
+    rng = np.random.default_rng(seed)
+    size = int(np.prod(shape))
+    return [rng.standard_normal(size, dtype=np.float32).reshape(shape) for _ in range(count)]
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def quantize_e4m3fn(x: np.ndarray):
+    """float32 -> (e4m3fn codes as uint8, per-tensor scale s as a Python float).
+
+    s = amax|x| / 448 computed in float32 (1.0 for an all-zero tensor);
+    codes = RNE(x / s) saturated to +-448.  The decoded value of a code times
+    s (exact in float64) is what the oracle consumes and what the kernel sees.
+    """
+    import torch
+
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    s = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+    y = torch.from_numpy(x / s).clamp_(-E4M3_MAX, E4M3_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, float(s)
+
+
+@dataclass
+class Inputs:
+    """Storage-format inputs for one workload.
+
+    q, k, v, dout: numpy arrays in the storage format (float32, uint16 bf16
+    bits, or uint8 e4m3fn codes).  descale: per-tensor (q, k, v) scales for
+    fp8, else 1.0.  dout is None for forward-only workloads.
+    """
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    dout: np.ndarray | None
+    descale: tuple
+    dtype: str
+
+
+def make_inputs(shape, dtype: str, seed: int = 42, with_dout: bool = True) -> Inputs:
+    q, k, v, *rest = draw_f32(shape, seed, 4 if with_dout else 3)
+    do = rest[0] if rest else None
+    if dtype == "fp32":
+        return Inputs(q, k, v, do if with_dout else None, (1.0, 1.0, 1.0), dtype)
+    if dtype == "bf16":
+        return Inputs(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v),
+                      to_bf16_bits(do) if with_dout else None, (1.0, 1.0, 1.0), dtype)
+    if dtype == "fp8":
+        (cq, sq), (ck, sk), (cv, sv) = (quantize_e4m3fn(t) for t in (q, k, v))
+        return Inputs(cq, ck, cv, None, (sq, sk, sv), dtype)
+    raise ValueError(f"unknown dtype {dtype!r}")
