@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: the
+forward (fa_fwd) and the three backward stages (fa_bwd_delta, fa_bwd_dkdv,
+fa_bwd_dq -- exactly what fa_bwd enqueues), on the bf16 causal workload
+B=2, H=16, N=4096, d=128 unless --workload says otherwise.  Inputs are resident
+in device memory before the timed region starts.  Each kernel is bracketed by
+HIP events on the stream it runs on, so per-kernel durations are measured live.
+
+After the timed steps the forward-only workloads (bf16 causal N=8192 d=128,
+bf16 N=2048 d=64, fp8 N=16384 d=128) are timed the same way and reported in
+the same JSON line, and the CPU oracle is timed on a bounded sample of the
+main workload on this host's cores.
+
+Prints ONE JSON line.  Only N=1 GPU is supported (--gpus > 1 exits).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "fp32": 157.3}  # dense, 256 CU x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOPS (bf16, fp8) and % of MI355X MFMA peak"
+MAIN = "bf16_causal_fwdbwd_b2h16n4096d128"
+EXTRA = ["bf16_causal_fwd_b2h32n8192d128", "bf16_fwd_b4h16n2048d64", "fp8_fwd_b1h32n16384d128"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def device_inputs(w, with_dout):
+    import torch
+
+    import fa_inputs
+
+    inp = fa_inputs.make_inputs(w.shape, w.dtype, seed=42, with_dout=with_dout)
+
+    def dev(a):
+        t = torch.from_numpy(a)
+        if w.dtype == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.cuda()
+
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    do = dev(inp.dout) if with_dout else None
+    return inp, q, k, v, do
+
+
+def algorithmic_work(w):
+    """Per-stage algorithmic FLOPs (bytes for the delta kernel)."""
+    import exact_io_aware_11_amd as fa
+
+    B, H, N, d, c = w.B, w.H, w.N, w.d, w.causal
+    per_product = 2.0 * B * H * N * N * d / (2 if c else 1)
+    elt = {"fp32": 4, "bf16": 2, "fp8": 1}[w.dtype]
+    return {
+        "fwd": fa.flops_fwd(B, H, N, d, c),
+        # dK/dV kernel: S recompute, dV, dP, dK; dQ kernel: the dQ product
+        "dkdv": 4 * per_product,
+        "dq": 1 * per_product,
+        # delta kernel: reads O and dO, writes one float per row
+        "delta_bytes": 2.0 * B * H * N * d * elt + 4.0 * B * H * N,
+    }
+
+
+def time_main(w, steps, warmup):
+    import torch
+
+    import exact_io_aware_11_amd as fa
+
+    inp, q, k, v, do = device_inputs(w, w.backward)
+    B, H, N, d = w.shape
+    odt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    o = torch.empty((B, H, N, d), dtype=odt, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    if w.backward:
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device="cuda")
+    stages = ["fwd"] + (["delta", "dkdv", "dq"] if w.backward else [])
+
+    def step(ev):
+        ev[0].record()
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, descale=inp.descale)
+        ev[1].record()
+        if w.backward:
+            args = (q, k, v, o, do, lse, dq, dk, dv, ws, w.scale, w.causal)
+            fa.fa_bwd_delta(*args)
+            ev[2].record()
+            fa.fa_bwd_dkdv(*args)
+            ev[3].record()
+            fa.fa_bwd_dq(*args)
+            ev[4].record()
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+
+    for _ in range(warmup):
+        step(events())
+    torch.cuda.synchronize()
+    evs = [events() for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    per = {s: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i, s in enumerate(stages)}
+    return total_ms / steps, wall, per
+
+
+def time_fwd_only(w, reps, warmup):
+    import torch
+
+    import exact_io_aware_11_amd as fa
+
+    inp, q, k, v, _ = device_inputs(w, False)
+    B, H, N, d = w.shape
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16 if w.dtype != "fp32" else torch.float32,
+                    device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, descale=inp.descale)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, descale=inp.descale)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    mean = sum(ms) / len(ms)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return mean, ms[len(ms) // 2]
+
+
+def cpu_baseline(w, max_heads):
+    """The oracle as it stands on a bounded sample: whole heads of the workload."""
+    import numpy as np
+
+    import exact_io_aware_11_amd as fa
+    import fa_inputs
+    import oracle
+
+    oracle.build(force=False)
+    inp = fa_inputs.make_inputs((1, max_heads, w.N, w.d), w.dtype, seed=42,
+                                with_dout=w.backward)
+
+    def exact(a, s=1.0):
+        if w.dtype == "fp32":
+            return a.astype(np.float64)
+        if w.dtype == "bf16":
+            return oracle.decode_bf16(a)
+        return oracle.decode_e4m3fn(a, s)
+
+    qs, ks, vs = (exact(x, s) for x, s in zip((inp.q, inp.k, inp.v), inp.descale))
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.attn_fwd(qs, ks, vs, w.scale, w.causal, nthreads=threads)
+    flops = fa.flops_fwd(1, max_heads, w.N, w.d, w.causal)
+    if w.backward:
+        oracle.attn_bwd(qs, ks, vs, exact(inp.dout), w.scale, w.causal, nthreads=threads)
+        flops += fa.flops_bwd(1, max_heads, w.N, w.d, w.causal)
+    sec = time.perf_counter() - t0
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(sec, 3),
+            "sample": f"{max_heads} of {w.B * w.H} heads at full N={w.N}, d={w.d} "
+                      f"({'fwd+bwd' if w.backward else 'fwd'}), float64 naive oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=MAIN)
+    ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: every (batch, head) is independent, so "
+              "several GPUs would each run this same kernel on their share of heads; "
+              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_11_amd as fa  # noqa: F401  (fails loudly without libfa.so)
+    import fa_inputs
+
+    w = fa_inputs.WORKLOADS[args.workload]
+    log(f"workload {w.name} steps={args.steps} warmup={args.warmup}")
+    ms, wall, per = time_main(w, args.steps, args.warmup)
+    work = algorithmic_work(w)
+    total_flops = work["fwd"] + (work["dkdv"] + work["dq"] if w.backward else 0.0)
+    peak = PEAK_TFLOPS[w.dtype]
+    kernels = {}
+    for s, t in per.items():
+        if s == "delta":
+            gbs = work["delta_bytes"] / (t * 1e-3) / 1e9
+            kernels[s] = {"ms": round(t, 4), "GB/s": round(gbs, 1),
+                          "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        else:
+            tf = work[s] / (t * 1e-3) / 1e12
+            kernels[s] = {"ms": round(t, 4), "TFLOP/s": round(tf, 1), "frac": round(tf / peak, 4)}
+    dom = max(per, key=per.get)
+    if dom == "delta":
+        ach = work["delta_bytes"] / (per[dom] * 1e-3) / 1e9
+        roof = {"kernel": "delta", "bound": "hbm", "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    else:
+        ach = work[dom] / (per[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
+    roof["traffic"] = None
+    value = total_flops / (ms * 1e-3) / 1e12
+    log(f"step {ms:.3f} ms  {value:.1f} TFLOP/s  kernels {kernels}")
+
+    extra = {}
+    if not args.no_extra:
+        for name in EXTRA:
+            if name == w.name:
+                continue
+            x = fa_inputs.WORKLOADS[name]
+            mean, med = time_fwd_only(x, reps=max(10, args.steps // 2), warmup=3)
+            tf = fa.flops_fwd(x.B, x.H, x.N, x.d, x.causal) / (mean * 1e-3) / 1e12
+            extra[name] = {"ms": round(mean, 4), "ms_median": round(med, 4),
+                           "TFLOP/s": round(tf, 1),
+                           "frac_of_peak": round(tf / PEAK_TFLOPS[x.dtype], 4),
+                           "peak": PEAK_TFLOPS[x.dtype]}
+            log(f"{name}: {mean:.3f} ms {tf:.1f} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(w, args.cpu_heads)
+        log(f"cpu oracle: {cpu}")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic: N(0,1) float32 draws, seed 42, cast to the "
+                                  "workload's format",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "passes": "fwd+bwd" if w.backward else "fwd",
+                   "scale": w.scale, "parallelism": "single GPU"},
+        "frac_of_peak": round(value / peak, 4),
+        "kernels": kernels,
+        "roofline": roof,
+        "forward_workloads": extra,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,120 @@
+"""Argument marshalling from torch tensors to the C ABI (include/fa.h)."""
+from __future__ import annotations
+
+from ._lib import FA_BF16, FA_FP8_E4M3, FA_FP32, FA_OK, FAError, lib
+
+
+def dtype_code(t) -> int:
+    """fa_dtype of a tensor: float32, bfloat16, or e4m3fn codes (float8_e4m3fn or uint8)."""
+    import torch
+
+    if t.dtype == torch.float32:
+        return FA_FP32
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return FA_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _stream_handle(stream) -> int:
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("expected a [B, H, N, d] tensor")
+    return tuple(int(x) for x in q.shape)
+
+
+def _check_like(name, t, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, descale=(1.0, 1.0, 1.0), stream=None):
+    """Enqueue the forward pass.  Writes o ([B,H,N,d]) and lse ([B,H,N] float32)."""
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_like(name, t, (B, H, N, d))
+    _check_like("lse", lse, (B, H, N))
+    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    B, H, N, d, float(scale), int(bool(causal)), dtype_code(q),
+                    float(descale[0]), float(descale[1]), float(descale[2]),
+                    _stream_handle(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd: " + fa_status_string(st))
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(lib.fa_bwd_workspace_size(B, H, N, d))
+
+
+def _bwd_call(fn_name, q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream):
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _check_like(name, t, (B, H, N, d))
+    _check_like("lse", lse, (B, H, N))
+    nbytes = workspace.numel() * workspace.element_size()
+    st = getattr(lib, fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), workspace.data_ptr(), nbytes, B, H, N, d,
+                               float(scale), int(bool(causal)), dtype_code(q),
+                               _stream_handle(stream))
+    if st != FA_OK:
+        raise FAError(st, f"{fn_name}: " + fa_status_string(st))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale: float, causal: bool,
+           stream=None):
+    """Enqueue the backward pass.  Writes dq, dk, dv; workspace (uint8 device
+    tensor of fa_bwd_workspace_size bytes) receives delta in its first B*H*N floats."""
+    _bwd_call("fa_bwd", q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream)
+
+
+def fa_bwd_delta(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream=None):
+    """Stage 1 of fa_bwd: delta into the workspace."""
+    _bwd_call("fa_bwd_delta", q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal,
+              stream)
+
+
+def fa_bwd_dkdv(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream=None):
+    """Stage 2 of fa_bwd: dK and dV."""
+    _bwd_call("fa_bwd_dkdv", q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal,
+              stream)
+
+
+def fa_bwd_dq(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream=None):
+    """Stage 3 of fa_bwd: dQ."""
+    _bwd_call("fa_bwd_dq", q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream)
+
+
+def fa_status_string(status: int) -> str:
+    return lib.fa_status_string(int(status)).decode()
+
+
+def flops_fwd(B, H, N, d, causal) -> float:
+    """Algorithmic forward FLOPs: 4 B H N^2 d, halved under the causal mask."""
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def flops_bwd(B, H, N, d, causal) -> float:
+    """Algorithmic backward FLOPs: the five N x N x d products (S recompute, dV,
+    dP, dQ, dK), 10 B H N^2 d, halved under the causal mask."""
+    f = 10.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+__all__ = ["FA_FP32", "FA_BF16", "FA_FP8_E4M3", "dtype_code", "fa_fwd", "fa_bwd",
+           "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
+           "fa_bwd_workspace_size", "fa_status_string", "flops_fwd", "flops_bwd"]

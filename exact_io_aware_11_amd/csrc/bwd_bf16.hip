@@ -1,0 +1,366 @@
+// Backward attention, bfloat16 inputs and gradients, float32 accumulation,
+// gfx950 MFMA.
+//
+// What it computes ("FlashAttention-1: eliminating IO", section 10.2.4): the
+// probabilities are recomputed tile by tile from the saved log-sum-exp,
+// P = exp(scale Q K^T - LSE), never stored; with delta_i = dO_i . O_i,
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),
+//   dK = scale dS^T Q,  dQ = scale dS K.
+//
+// Two kernels after the delta kernel, on one stream, no atomics:
+//  * dK/dV: one workgroup per (batch, head, block of 128 keys); each wave
+//    holds 32 keys' K and V rows in registers and scans the query tiles of 64
+//    rows that can see them (all, or those at or after the keys when causal).
+//    S = Q K^T and dP = dO V^T come out with one key per lane column; P and
+//    dS are then fed, converted to bf16, straight back as the B operand of
+//    dV^T = dO^T P and dK^T = Q^T dS, whose A operands (dO^T, Q^T) are read
+//    from the row-major LDS tiles with ds_read_b64_tr_b16.
+//  * dQ: one workgroup per (batch, head, block of 128 queries); each wave
+//    holds 32 queries' Q and dO rows in registers and scans the key tiles.
+//    S^T = K Q^T and dP^T = V dO^T give one query per lane column (so LSE and
+//    delta are per-lane scalars); dS^T feeds dQ^T = K^T dS^T with K^T read by
+//    the transposing LDS read.
+// Recomputing S and dP in the dQ pass costs two extra matrix products over
+// the five the method needs; it keeps every output written exactly once.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int N, uint32_t n_kblk, uint32_t total, float scale,
+    float scale_log2) {
+  constexpr int BN = 128, BM = 64, CH = D / 8, TILE = BM * D;
+  constexpr int PER = BM * CH / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];      // [buffer][LSE*log2e, delta]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  uint32_t bh, kblk;
+  map_block(blockIdx.x, n_kblk, total, false, bh, kblk);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* dOh = dO + head;
+  const float* LSEh = LSE + (size_t)bh * N;
+  const float* Dh = Delta + (size_t)bh * N;
+
+  const int k0 = (int)kblk * BN + wave * 32;
+  const int kcol = k0 + r32;  // this lane's key (C-layout column)
+
+  // K and V rows as the B operands of S = Q K^T and dP = dO V^T.
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    if (kcol < N) {
+      kf[t] = *reinterpret_cast<const bf16x8*>(K + head + (size_t)kcol * D + 16 * t + 8 * g);
+      vf[t] = *reinterpret_cast<const bf16x8*>(V + head + (size_t)kcol * D + 16 * t + 8 * g);
+    } else {
+      kf[t] = bf16x8{};
+      vf[t] = bf16x8{};
+    }
+  }
+
+  const int n_it = (N + BM - 1) / BM;
+  const int it0 = CAUSAL ? ((int)kblk * BN) / BM : 0;
+
+  uint4 qreg[PER], oreg[PER];
+  float sreg = 0.f;
+  auto gload = [&](int it) {
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int c = tid + 256 * x, row = c / CH, ch = c % CH, q = it * BM + row;
+      if (q < N) {
+        qreg[x] = *reinterpret_cast<const uint4*>(Qh + (size_t)q * D + ch * 8);
+        oreg[x] = *reinterpret_cast<const uint4*>(dOh + (size_t)q * D + ch * 8);
+      } else {
+        qreg[x] = make_uint4(0, 0, 0, 0);
+        oreg[x] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (tid < 2 * BM) {
+      const int q = it * BM + (tid & (BM - 1));
+      sreg = q < N ? (tid < BM ? LSEh[q] * kLog2e : Dh[q]) : 0.f;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int c = tid + 256 * x, row = c / CH, ch = c % CH;
+      *reinterpret_cast<uint4*>(&lds[buf][0][tile_off<D>(row, ch)]) = qreg[x];
+      *reinterpret_cast<uint4*>(&lds[buf][1][tile_off<D>(row, ch)]) = oreg[x];
+    }
+    if (tid < 2 * BM) stat[buf][tid / BM][tid & (BM - 1)] = sreg;
+  };
+
+  const int tr_src = lane & 15, tr_r = tr_src >> 2, tr_c = tr_src & 3;
+  const int tr_n0 = 16 * ((lane >> 4) & 1);
+
+  f32x16 adk[D / 32], adv[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) {
+    adk[cb] = f32x16{};
+    adv[cb] = f32x16{};
+  }
+
+  if (it0 < n_it) {
+    gload(it0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int it = it0; it < n_it; ++it) {
+    const int buf = (it - it0) & 1;
+    if (it + 1 < n_it) gload(it + 1);
+    const int qbase = it * BM;
+    const bool active = !CAUSAL || qbase + BM - 1 >= k0;
+    if (active) {
+      const uint16_t* Qt = lds[buf][0];
+      const uint16_t* Ot = lds[buf][1];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const int arow = 32 * qb + r32;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          s = mfma_bf16(lds_read_b128(Qt + tile_off<D>(arow, 2 * t + g)), kf[t], s);
+          dp = mfma_bf16(lds_read_b128(Ot + tile_off<D>(arow, 2 * t + g)), vf[t], dp);
+        }
+        const int qrow0 = qbase + 32 * qb;
+        const bool need_mask = (qrow0 + 32 > N) || (k0 + 32 > N) || (CAUSAL && k0 + 31 > qrow0);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int rr = 32 * qb + 8 * q4 + 4 * g;
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stat[buf][0][rr]);
+          const f32x4 dl = *reinterpret_cast<const f32x4*>(&stat[buf][1][rr]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q4 + e;
+            float p = exp2_fast(fmaf(s[i], scale_log2, -l2[e]));
+            if (need_mask) {
+              const int q = qbase + rr + e;
+              if (q >= N || kcol >= N || (CAUSAL && kcol > q)) p = 0.f;
+            }
+            s[i] = p;
+            dp[i] = p * (dp[i] - dl[e]);
+          }
+        }
+        bf16x8 pb[2], db[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          pb[h] = to_bf16x8(s, 8 * h);
+          db[h] = to_bf16x8(dp, 8 * h);
+        }
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) {
+          const int d = 32 * cb + tr_n0 + 4 * tr_c;
+          const int ch = d >> 3, sub = d & 7;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int r0 = 32 * qb + 16 * h + 4 * g + tr_r, r1 = r0 + 8;
+            const bf16x8 ao = concat(lds_read_tr16(Ot + tile_off<D>(r0, ch) + sub),
+                                     lds_read_tr16(Ot + tile_off<D>(r1, ch) + sub));
+            adv[cb] = mfma_bf16(ao, pb[h], adv[cb]);
+            const bf16x8 aq = concat(lds_read_tr16(Qt + tile_off<D>(r0, ch) + sub),
+                                     lds_read_tr16(Qt + tile_off<D>(r1, ch) + sub));
+            adk[cb] = mfma_bf16(aq, db[h], adk[cb]);
+          }
+        }
+      }
+    }
+    if (it + 1 < n_it) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (kcol < N) {
+    uint16_t* dKrow = dK + head + (size_t)kcol * D;
+    uint16_t* dVrow = dV + head + (size_t)kcol * D;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = (__bf16)(adk[cb][4 * q4 + e] * scale);
+          b[e] = (__bf16)adv[cb][4 * q4 + e];
+        }
+        *reinterpret_cast<bf16x4*>(dKrow + 32 * cb + 8 * q4 + 4 * g) = a;
+        *reinterpret_cast<bf16x4*>(dVrow + 32 * cb + 8 * q4 + 4 * g) = b;
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dq_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
+    int N, uint32_t n_qblk, uint32_t total, float scale, float scale_log2) {
+  constexpr int BM = 128, BN = 64, CH = D / 8, TILE = BN * D;
+  constexpr int PER = BN * CH / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [buffer][K, V]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  uint32_t bh, qblk;
+  map_block(blockIdx.x, n_qblk, total, CAUSAL, bh, qblk);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+
+  const int q0 = (int)qblk * BM + wave * 32;
+  const int qrow = q0 + r32;
+
+  bf16x8 qf[D / 16], of[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    if (qrow < N) {
+      qf[t] = *reinterpret_cast<const bf16x8*>(Q + head + (size_t)qrow * D + 16 * t + 8 * g);
+      of[t] = *reinterpret_cast<const bf16x8*>(dO + head + (size_t)qrow * D + 16 * t + 8 * g);
+    } else {
+      qf[t] = bf16x8{};
+      of[t] = bf16x8{};
+    }
+  }
+  const float lse2 = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  const float del = qrow < N ? Delta[(size_t)bh * N + qrow] : 0.f;
+
+  const int kv_end = CAUSAL ? min(N, (int)qblk * BM + BM) : N;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+
+  uint4 kreg[PER], vreg[PER];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int c = tid + 256 * x, row = c / CH, ch = c % CH, key = j * BN + row;
+      if (key < N) {
+        kreg[x] = *reinterpret_cast<const uint4*>(Kh + (size_t)key * D + ch * 8);
+        vreg[x] = *reinterpret_cast<const uint4*>(Vh + (size_t)key * D + ch * 8);
+      } else {
+        kreg[x] = make_uint4(0, 0, 0, 0);
+        vreg[x] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int c = tid + 256 * x, row = c / CH, ch = c % CH;
+      *reinterpret_cast<uint4*>(&lds[buf][0][tile_off<D>(row, ch)]) = kreg[x];
+      *reinterpret_cast<uint4*>(&lds[buf][1][tile_off<D>(row, ch)]) = vreg[x];
+    }
+  };
+
+  const int tr_src = lane & 15, tr_r = tr_src >> 2, tr_c = tr_src & 3;
+  const int tr_n0 = 16 * ((lane >> 4) & 1);
+
+  f32x16 adq[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) adq[cb] = f32x16{};
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < n_tiles) gload(j + 1);
+    const int key0 = j * BN;
+    const bool active = !CAUSAL || key0 <= q0 + 31;
+    if (active) {
+      const uint16_t* Kt = lds[buf][0];
+      const uint16_t* Vt = lds[buf][1];
+      const bool need_mask = (key0 + BN > N) || (q0 + 32 > N) || (CAUSAL && key0 + BN - 1 > q0);
+      bf16x8 db[2][2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const int krow = 32 * b + r32;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          s = mfma_bf16(lds_read_b128(Kt + tile_off<D>(krow, 2 * t + g)), qf[t], s);
+          dp = mfma_bf16(lds_read_b128(Vt + tile_off<D>(krow, 2 * t + g)), of[t], dp);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = exp2_fast(fmaf(s[i], scale_log2, -lse2));
+          if (need_mask) {
+            const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key >= N || qrow >= N || (CAUSAL && key > qrow)) p = 0.f;
+          }
+          dp[i] = p * (dp[i] - del);
+        }
+        db[b][0] = to_bf16x8(dp, 0);
+        db[b][1] = to_bf16x8(dp, 8);
+      }
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) {
+        const int d = 32 * cb + tr_n0 + 4 * tr_c;
+        const int ch = d >> 3, sub = d & 7;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int r0 = 32 * b + 16 * h + 4 * g + tr_r, r1 = r0 + 8;
+            const bf16x8 ak = concat(lds_read_tr16(Kt + tile_off<D>(r0, ch) + sub),
+                                     lds_read_tr16(Kt + tile_off<D>(r1, ch) + sub));
+            adq[cb] = mfma_bf16(ak, db[b][h], adq[cb]);
+          }
+      }
+    }
+    if (j + 1 < n_tiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qrow < N) {
+    uint16_t* dQrow = dQ + head + (size_t)qrow * D;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(adq[cb][4 * q4 + e] * scale);
+        *reinterpret_cast<bf16x4*>(dQrow + 32 * cb + 8 * q4 + 4 * g) = v;
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t dkdv_bf16_t(const BwdArgs& a) {
+  const uint32_t n_kblk = (uint32_t)((a.N + 127) / 128);
+  const uint32_t total = (uint32_t)(a.BH * n_kblk);
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                     a.N, n_kblk, total, a.scale, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t dq_bf16_t(const BwdArgs& a) {
+  const uint32_t n_qblk = (uint32_t)((a.N + 127) / 128);
+  const uint32_t total = (uint32_t)(a.BH * n_qblk);
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.N, n_qblk,
+                     total, a.scale, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+hipError_t launch_dkdv_bf16(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? dkdv_bf16_t<64, true>(a) : dkdv_bf16_t<64, false>(a);
+  return a.causal ? dkdv_bf16_t<128, true>(a) : dkdv_bf16_t<128, false>(a);
+}
+
+hipError_t launch_dq_bf16(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? dq_bf16_t<64, true>(a) : dq_bf16_t<64, false>(a);
+  return a.causal ? dq_bf16_t<128, true>(a) : dq_bf16_t<128, false>(a);
+}
+
+}  // namespace fa

@@ -1,0 +1,332 @@
+// float32 attention kernels (forward, delta, dK/dV, dQ) and the delta kernel
+// for both float32 and bfloat16.
+//
+// What they compute follows "FlashAttention-1: eliminating IO": the forward
+// of sections 10.2.1-10.2.3 (running max m, running sum l, unnormalised
+// accumulator rescaled by alpha = exp(m_old - m_new), one final division,
+// LSE = m + ln l), and the recompute backward of section 10.2.4
+// (P = exp(S - LSE), dV = P^T dO, dP = dO V^T, dS = P o (dP - delta),
+// dQ = scale dS K, dK = scale dS^T Q, delta_i = dO_i . O_i).
+//
+// Tiles are Br = Bc = 32 rows, the block sizes of the FA1 page's examples
+// (sections 10.2.3 and 10.2.4).  These kernels serve float32 problems, which
+// the pages use for their exactness checks; float32 on gfx950 has the same
+// peak on the vector ALUs as on the matrix cores, so they are plain
+// LDS-tiled FMA kernels with exact expf/logf.  One workgroup of 256 threads
+// per (batch, head, 32-row block); 8 threads share a row.
+#include <math.h>
+
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kBR = 32, kBC = 32;
+
+__device__ __forceinline__ float group8_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 1, 8));
+  x = fmaxf(x, __shfl_xor(x, 2, 8));
+  x = fmaxf(x, __shfl_xor(x, 4, 8));
+  return x;
+}
+__device__ __forceinline__ float group8_sum(float x) {
+  x += __shfl_xor(x, 1, 8);
+  x += __shfl_xor(x, 2, 8);
+  x += __shfl_xor(x, 4, 8);
+  return x;
+}
+
+// Rows [row0, row0 + rows) of a [N][D] matrix into an LDS tile, zero past N.
+template <int D, int LD>
+__device__ __forceinline__ void load_rows(float (*dst)[LD], const float* src, int row0, int rows,
+                                          int N) {
+  for (int x = threadIdx.x; x < rows * D; x += 256) {
+    const int rr = x / D, c = x - rr * D, row = row0 + rr;
+    dst[rr][c] = row < N ? src[(size_t)row * D + c] : 0.f;
+  }
+}
+
+}  // namespace
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q,
+                                                      const float* __restrict__ K,
+                                                      const float* __restrict__ V,
+                                                      float* __restrict__ O,
+                                                      float* __restrict__ LSE, int N, float scale) {
+  constexpr int DS = D / 8;
+  __shared__ float Qs[kBR][D + 1], Ks[kBC][D + 1], Vs[kBC][D], Ps[kBR][kBC + 1];
+  const int tid = threadIdx.x, r = tid >> 3, sub = tid & 7;
+  const int nq = (N + kBR - 1) / kBR;
+  const size_t bh = blockIdx.x / nq;
+  const int q0 = (int)(blockIdx.x - bh * nq) * kBR, qrow = q0 + r;
+  const size_t head = bh * (size_t)N * D;
+  load_rows<D, D + 1>(Qs, Q + head, q0, kBR, N);
+  float acc[DS];
+#pragma unroll
+  for (int x = 0; x < DS; ++x) acc[x] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
+  for (int k0 = 0; k0 < kv_end; k0 += kBC) {
+    __syncthreads();
+    load_rows<D, D + 1>(Ks, K + head, k0, kBC, N);
+    load_rows<D, D>(Vs, V + head, k0, kBC, N);
+    __syncthreads();
+    float s[4], mt = -INFINITY;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int c = sub + 8 * cc, key = k0 + c;
+      float dot = 0.f;
+      for (int x = 0; x < D; ++x) dot = fmaf(Qs[r][x], Ks[c][x], dot);
+      s[cc] = (key < N && (!CAUSAL || key <= qrow)) ? dot * scale : -INFINITY;
+      mt = fmaxf(mt, s[cc]);
+    }
+    mt = group8_max(mt);
+    const float m_new = fmaxf(m, mt);
+    const float alpha = expf(m - m_new);
+    float rs = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const float p = expf(s[cc] - m_new);
+      Ps[r][sub + 8 * cc] = p;
+      rs += p;
+    }
+    rs = group8_sum(rs);
+    l = l * alpha + rs;
+    m = m_new;
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < DS; ++x) {
+      const int d = sub * DS + x;
+      float a = acc[x] * alpha;
+      for (int c = 0; c < kBC; ++c) a = fmaf(Ps[r][c], Vs[c][d], a);
+      acc[x] = a;
+    }
+  }
+  if (qrow < N) {
+    float* Orow = O + head + (size_t)qrow * D + sub * DS;
+#pragma unroll
+    for (int x = 0; x < DS; ++x) Orow[x] = acc[x] / l;
+    if (sub == 0) LSE[bh * N + qrow] = m + logf(l);
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    float* __restrict__ dK, float* __restrict__ dV, int N, float scale) {
+  constexpr int DS = D / 8;
+  __shared__ float Ks[kBC][D + 1], Vs[kBC][D + 1], Qs[kBR][D + 1], dOs[kBR][D + 1];
+  __shared__ float Ps[kBR][kBC + 1], dSs[kBR][kBC + 1], lse_s[kBR], del_s[kBR];
+  const int tid = threadIdx.x, r = tid >> 3, sub = tid & 7;
+  const int nk = (N + kBC - 1) / kBC;
+  const size_t bh = blockIdx.x / nk;
+  const int k0 = (int)(blockIdx.x - bh * nk) * kBC;
+  const size_t head = bh * (size_t)N * D;
+  load_rows<D, D + 1>(Ks, K + head, k0, kBC, N);
+  load_rows<D, D + 1>(Vs, V + head, k0, kBC, N);
+  float dk[DS], dv[DS];
+#pragma unroll
+  for (int x = 0; x < DS; ++x) dk[x] = dv[x] = 0.f;
+  const int q_start = CAUSAL ? k0 : 0;  // earlier query tiles see none of these keys
+  for (int q0 = q_start; q0 < N; q0 += kBR) {
+    __syncthreads();
+    load_rows<D, D + 1>(Qs, Q + head, q0, kBR, N);
+    load_rows<D, D + 1>(dOs, dO + head, q0, kBR, N);
+    if (tid < kBR) {
+      const int q = q0 + tid;
+      lse_s[tid] = q < N ? LSE[bh * N + q] : 0.f;
+      del_s[tid] = q < N ? Delta[bh * N + q] : 0.f;
+    }
+    __syncthreads();
+    const int q = q0 + r;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int c = sub + 8 * cc, key = k0 + c;
+      float sd = 0.f, dpd = 0.f;
+      for (int x = 0; x < D; ++x) {
+        sd = fmaf(Qs[r][x], Ks[c][x], sd);
+        dpd = fmaf(dOs[r][x], Vs[c][x], dpd);
+      }
+      const bool valid = key < N && q < N && (!CAUSAL || key <= q);
+      const float p = valid ? expf(sd * scale - lse_s[r]) : 0.f;
+      Ps[r][c] = p;
+      dSs[r][c] = p * (dpd - del_s[r]);
+    }
+    __syncthreads();
+    const int kk = r;  // this thread's key row for accumulation
+#pragma unroll
+    for (int x = 0; x < DS; ++x) {
+      const int d = sub * DS + x;
+      float a = dv[x], b = dk[x];
+      for (int rr = 0; rr < kBR; ++rr) {
+        a = fmaf(Ps[rr][kk], dOs[rr][d], a);
+        b = fmaf(dSs[rr][kk], Qs[rr][d], b);
+      }
+      dv[x] = a;
+      dk[x] = b;
+    }
+  }
+  const int key = k0 + r;
+  if (key < N) {
+#pragma unroll
+    for (int x = 0; x < DS; ++x) {
+      dK[head + (size_t)key * D + sub * DS + x] = dk[x] * scale;
+      dV[head + (size_t)key * D + sub * DS + x] = dv[x];
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    float* __restrict__ dQ, int N, float scale) {
+  constexpr int DS = D / 8;
+  __shared__ float Qs[kBR][D + 1], dOs[kBR][D + 1], Ks[kBC][D + 1], Vs[kBC][D + 1];
+  __shared__ float dSs[kBR][kBC + 1];
+  const int tid = threadIdx.x, r = tid >> 3, sub = tid & 7;
+  const int nq = (N + kBR - 1) / kBR;
+  const size_t bh = blockIdx.x / nq;
+  const int q0 = (int)(blockIdx.x - bh * nq) * kBR, q = q0 + r;
+  const size_t head = bh * (size_t)N * D;
+  load_rows<D, D + 1>(Qs, Q + head, q0, kBR, N);
+  load_rows<D, D + 1>(dOs, dO + head, q0, kBR, N);
+  const float lse = q < N ? LSE[bh * N + q] : 0.f;
+  const float del = q < N ? Delta[bh * N + q] : 0.f;
+  float dq[DS];
+#pragma unroll
+  for (int x = 0; x < DS; ++x) dq[x] = 0.f;
+  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
+  for (int k0 = 0; k0 < kv_end; k0 += kBC) {
+    __syncthreads();
+    load_rows<D, D + 1>(Ks, K + head, k0, kBC, N);
+    load_rows<D, D + 1>(Vs, V + head, k0, kBC, N);
+    __syncthreads();
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int c = sub + 8 * cc, key = k0 + c;
+      float sd = 0.f, dpd = 0.f;
+      for (int x = 0; x < D; ++x) {
+        sd = fmaf(Qs[r][x], Ks[c][x], sd);
+        dpd = fmaf(dOs[r][x], Vs[c][x], dpd);
+      }
+      const bool valid = key < N && q < N && (!CAUSAL || key <= q);
+      const float p = valid ? expf(sd * scale - lse) : 0.f;
+      dSs[r][c] = p * (dpd - del);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < DS; ++x) {
+      const int d = sub * DS + x;
+      float a = dq[x];
+      for (int c = 0; c < kBC; ++c) a = fmaf(dSs[r][c], Ks[c][d], a);
+      dq[x] = a;
+    }
+  }
+  if (q < N) {
+#pragma unroll
+    for (int x = 0; x < DS; ++x) dQ[head + (size_t)q * D + sub * DS + x] = dq[x] * scale;
+  }
+}
+
+// delta_i = sum_c dO_ic O_ic (FA1 page, section 10.2.4), float32 result.
+// 16 lanes per row, 16 rows per workgroup, 16-byte loads.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void delta_kernel(const void* __restrict__ Ov,
+                                                    const void* __restrict__ dOv,
+                                                    float* __restrict__ delta, long rows) {
+  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    if constexpr (BF16) {
+      constexpr int CH = D / 8;
+      const uint4* o = reinterpret_cast<const uint4*>((const uint16_t*)Ov + row * D);
+      const uint4* g = reinterpret_cast<const uint4*>((const uint16_t*)dOv + row * D);
+      for (int c = sub; c < CH; c += 16) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, o[c]);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, g[c]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+      }
+    } else {
+      constexpr int CH = D / 4;
+      const float4* o = reinterpret_cast<const float4*>((const float*)Ov + row * D);
+      const float4* g = reinterpret_cast<const float4*>((const float*)dOv + row * D);
+      for (int c = sub; c < CH; c += 16) {
+        const float4 a = o[c], b = g[c];
+        acc = fmaf(a.x, b.x, acc);
+        acc = fmaf(a.y, b.y, acc);
+        acc = fmaf(a.z, b.z, acc);
+        acc = fmaf(a.w, b.w, acc);
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 8, 16);
+  acc += __shfl_xor(acc, 4, 16);
+  acc += __shfl_xor(acc, 2, 16);
+  acc += __shfl_xor(acc, 1, 16);
+  if (row < rows && sub == 0) delta[row] = acc;
+}
+
+hipError_t launch_delta(const BwdArgs& a, bool bf16) {
+  const long rows = a.BH * (long)a.N;
+  const dim3 grid((unsigned)((rows + 15) / 16));
+  if (bf16) {
+    if (a.d == 64) hipLaunchKernelGGL((delta_kernel<true, 64>), grid, dim3(256), 0, a.stream, a.o, a.dout, a.delta, rows);
+    else hipLaunchKernelGGL((delta_kernel<true, 128>), grid, dim3(256), 0, a.stream, a.o, a.dout, a.delta, rows);
+  } else {
+    if (a.d == 64) hipLaunchKernelGGL((delta_kernel<false, 64>), grid, dim3(256), 0, a.stream, a.o, a.dout, a.delta, rows);
+    else hipLaunchKernelGGL((delta_kernel<false, 128>), grid, dim3(256), 0, a.stream, a.o, a.dout, a.delta, rows);
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t fwd_f32_t(const FwdArgs& a) {
+  const long nq = (a.N + kBR - 1) / kBR;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nq)), dim3(256), 0,
+                     a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                     (float*)a.o, a.lse, a.N, a.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const FwdArgs& a) {
+  if (a.d == 64) return a.causal ? fwd_f32_t<64, true>(a) : fwd_f32_t<64, false>(a);
+  return a.causal ? fwd_f32_t<128, true>(a) : fwd_f32_t<128, false>(a);
+}
+
+template <int D, bool CAUSAL>
+static hipError_t dkdv_f32_t(const BwdArgs& a) {
+  const long nb = (a.N + kBC - 1) / kBC;
+  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nb)), dim3(256), 0,
+                     a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                     (const float*)a.dout, a.lse, a.delta, (float*)a.dk, (float*)a.dv, a.N,
+                     a.scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t dq_f32_t(const BwdArgs& a) {
+  const long nb = (a.N + kBR - 1) / kBR;
+  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nb)), dim3(256), 0,
+                     a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                     (const float*)a.dout, a.lse, a.delta, (float*)a.dq, a.N, a.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_dkdv_f32(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? dkdv_f32_t<64, true>(a) : dkdv_f32_t<64, false>(a);
+  return a.causal ? dkdv_f32_t<128, true>(a) : dkdv_f32_t<128, false>(a);
+}
+
+hipError_t launch_dq_f32(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? dq_f32_t<64, true>(a) : dq_f32_t<64, false>(a);
+  return a.causal ? dq_f32_t<128, true>(a) : dq_f32_t<128, false>(a);
+}
+
+}  // namespace fa

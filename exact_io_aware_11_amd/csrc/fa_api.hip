@@ -1,0 +1,169 @@
+// C ABI entry points: argument validation and dispatch to the gfx950 kernels.
+// Every check happens before any HIP call, so invalid arguments never launch
+// anything.  See include/fa.h for the contract.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr long kMaxElems = 1L << 40;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool finite_pos(float x) { return isfinite(x) && x > 0.f; }
+
+// Shared size checks.  Returns FA_OK and sets *empty when there is no work.
+fa_status check_sizes(int B, int H, int N, int d, bool* empty) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return d > 0 ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
+  const long bhn = (long)B * (long)H * (long)N;
+  *empty = bhn == 0;
+  if (bhn > kMaxElems / d) return FA_ERR_INVALID_ARG;
+  // one workgroup per 32 rows at most: keep the grid inside 32 bits
+  const long blocks = (long)B * (long)H * (((long)N + 31) / 32);
+  if (blocks > 0x7fffffffL) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+size_t ws_bytes(long BH, int N) {
+  const size_t delta = (size_t)BH * (size_t)N * sizeof(float);
+  return (delta + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, int dtype, float q_descale,
+                 float k_descale, float v_descale, void* stream) {
+  if (dtype != FA_FP32 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  bool empty = false;
+  fa_status st = check_sizes(B, H, N, d, &empty);
+  if (st != FA_OK) return st;
+  if (!finite_pos(scale)) return FA_ERR_INVALID_ARG;
+  if (dtype == FA_FP8_E4M3 &&
+      (!finite_pos(q_descale) || !finite_pos(k_descale) || !finite_pos(v_descale)))
+    return FA_ERR_INVALID_ARG;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_INVALID_ARG;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = (long)B * H;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  a.stream = (hipStream_t)stream;
+  hipError_t e;
+  switch (dtype) {
+    case FA_FP32: e = fa::launch_fwd_f32(a); break;
+    case FA_BF16: e = fa::launch_fwd_bf16(a); break;
+    default: e = fa::launch_fwd_fp8(a); break;
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  bool empty = false;
+  if (check_sizes(B, H, N, d, &empty) != FA_OK) return 0;
+  return ws_bytes((long)B * H, N);
+}
+
+}  // extern "C"
+
+namespace {
+
+enum { kStageDelta = 1, kStageDkDv = 2, kStageDq = 4 };
+
+fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                  int dtype, void* stream, int stages) {
+  if (dtype != FA_FP32 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  bool empty = false;
+  fa_status st = check_sizes(B, H, N, d, &empty);
+  if (st != FA_OK) return st;
+  if (dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
+  if (!finite_pos(scale)) return FA_ERR_INVALID_ARG;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 4))
+    return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_bytes((long)B * H, N)) return FA_ERR_INVALID_ARG;
+
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float*)workspace;
+  a.BH = (long)B * H;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.stream = (hipStream_t)stream;
+  const bool bf16 = dtype == FA_BF16;
+  hipError_t e = hipSuccess;
+  if (stages & kStageDelta) e = fa::launch_delta(a, bf16);
+  if (e == hipSuccess && (stages & kStageDkDv))
+    e = bf16 ? fa::launch_dkdv_bf16(a) : fa::launch_dkdv_f32(a);
+  if (e == hipSuccess && (stages & kStageDq)) e = bf16 ? fa::launch_dq_bf16(a) : fa::launch_dq_f32(a);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+#define FA_BWD_PARAMS                                                                           \
+  const void *q, const void *k, const void *v, const void *o, const void *dout,                 \
+      const float *lse, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes, \
+      int B, int H, int N, int d, float scale, int causal, int dtype, void *stream
+#define FA_BWD_ARGS                                                                          \
+  q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, scale, causal, \
+      dtype, stream
+
+fa_status fa_bwd(FA_BWD_PARAMS) {
+  return run_bwd(FA_BWD_ARGS, kStageDelta | kStageDkDv | kStageDq);
+}
+fa_status fa_bwd_delta(FA_BWD_PARAMS) { return run_bwd(FA_BWD_ARGS, kStageDelta); }
+fa_status fa_bwd_dkdv(FA_BWD_PARAMS) { return run_bwd(FA_BWD_ARGS, kStageDkDv); }
+fa_status fa_bwd_dq(FA_BWD_PARAMS) { return run_bwd(FA_BWD_ARGS, kStageDq); }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Matrix-core lane layouts used throughout (measured on gfx950 with an
+// in-bounds probe, and relied on by every kernel):
+//  v_mfma_f32_32x32x16_bf16  (A 32x16, B 16x32, C 32x32), lane l, g = l / 32:
+//    A: lane l holds A[l % 32][8g .. 8g+7]
+//    B: lane l holds B[8g .. 8g+7][l % 32]
+//    C: lane l element i holds C[8(i/4) + 4g + i%4][l % 32]
+//  Only the pairing of A's and B's k-slots matters to the product, so any
+//  permutation of k applied to both operands is free; the kernels use that to
+//  feed a C-layout tile straight back in as a B operand.
+//  ds_read_b64_tr_b16: within each group of 16 lanes, output lane j element r
+//    is element (j % 4) of the 8 bytes addressed by source lane 4r + j/4.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp8 (OCP e4m3fn) x fp8, K = 64 per instruction, unit block scales.
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max / sum of a value over lanes l and l ^ 32 (the two halves of a wave).
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16-byte LDS read of 8 bf16 (p points into a __shared__ array).
+__device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Transposing 8-byte LDS read (see the layout note at the top); p points
+// into a __shared__ array.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Round-to-nearest-even float -> bfloat16 of 8 consecutive accumulator values.
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& c, int first) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)c[first + e];
+  return r;
+}
+
+// acc + sum of 8 bf16 values (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2 p = {v[e], v[e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
+  }
+  return acc;
+}
+
+// Workgroup -> (head, row block) mapping.  Workgroups are dispatched to the 8
+// XCDs round-robin (id % 8), each XCD with its own L2.  When the grid divides
+// by 8, XCD x is given the contiguous range of logical blocks
+// [x * total/8, (x+1) * total/8), so the row blocks of one head run on one
+// XCD at the same time and share its L2 copy of that head's K and V.  With a
+// causal mask the heaviest row blocks (most visible keys) of a head go first.
+__device__ __forceinline__ void map_block(uint32_t w, uint32_t n_blk, uint32_t total,
+                                          bool heavy_first_reverse, uint32_t& bh, uint32_t& blk) {
+  uint32_t logical = w;
+  if ((total & 7u) == 0u) logical = (w & 7u) * (total >> 3) + (w >> 3);
+  bh = logical / n_blk;
+  blk = logical - bh * n_blk;
+  if (heavy_first_reverse) blk = n_blk - 1u - blk;
+}
+
+// 16-byte-chunk XOR swizzle of a [rows][D] bf16 tile in LDS.  Lanes that read
+// the same logical chunk of 16 consecutive rows hit 16 different bank groups.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return row & 15;
+  else return (row >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {  // element offset
+  return row * D + ((chunk ^ swz<D>(row)) << 3);
+}
+
+}  // namespace fa

@@ -1,0 +1,52 @@
+// Internal launcher interface between the C ABI (fa_api.hip) and the kernels.
+// Arguments are validated by the caller; launchers only pick an instantiation
+// and enqueue it on the given stream.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  long BH;  // batch * heads
+  int N, d;
+  float scale;
+  bool causal;
+  float q_descale, k_descale, v_descale;  // fp8 only
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [BH * N] inside the workspace
+  long BH;
+  int N, d;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_fp8(const FwdArgs& a);
+hipError_t launch_delta(const BwdArgs& a, bool bf16);
+hipError_t launch_dkdv_f32(const BwdArgs& a);
+hipError_t launch_dq_f32(const BwdArgs& a);
+hipError_t launch_dkdv_bf16(const BwdArgs& a);
+hipError_t launch_dq_bf16(const BwdArgs& a);
+
+}  // namespace fa

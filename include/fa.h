@@ -1,0 +1,126 @@
+/*
+ * fa.h -- C ABI of the exact, IO-aware attention library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention
+ *     S = scale * Q K^T,  P = softmax(S) row-wise,  O = P V
+ * tile by tile with an online softmax, so that S and P never reach device
+ * memory; it writes only O and one log-sum-exp per row.  The backward pass
+ * recomputes each P tile from that log-sum-exp and uses
+ * delta_i = rowsum(dO_i o O_i) to form dQ, dK and dV.
+ *
+ * Sources for what is computed:
+ *  - "FlashAttention-1: eliminating IO" (deep-learning-notes ch10.2):
+ *    section 10.2.1 (definition and safe softmax), section 10.2.2 (online
+ *    rescaling with alpha = exp(m_old - m_new)), section 10.2.3 (forward,
+ *    scale 1/sqrt(d)), section 10.2.4 (recompute backward, dS = P o (dP - delta),
+ *    delta_i = dO_i . O_i), section 10.2.5 (one workgroup per query block).
+ *  - "Flash Attention V1/V2/V3" explainer: V2 section (query-block work
+ *    partitioning, deferred normalisation, mask fused into the score stage) and
+ *    V3 section (FP8 inputs with FP32 accumulation and scaling factors).
+ *  - "5.4 FlashAttention (1/2/3)" reading notes, code 3-1 (running max,
+ *    alpha, unnormalised accumulator, one final division).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors Q, K, V, O, dO, dQ, dK, dV are contiguous row-major [B, H, N, d]
+ *    arrays (d innermost).  LSE and delta are contiguous [B, H, N] float32.
+ *  - Causal: key j is visible to query i iff j <= i (square attention).
+ *  - LSE_i = ln sum_j exp(S_ij) in the natural log of the scaled scores.
+ *  - All pointers are device pointers the caller owns.  The library allocates
+ *    nothing, keeps no mutable global state and never synchronises: work is
+ *    enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *    call returns.  Calls on different streams are independent.
+ *  - Supported head sizes d: 64 and 128.  Any N >= 1; B * H * N == 0 is a
+ *    no-op returning FA_OK.  Tensor pointers must be 16-byte aligned, LSE and
+ *    workspace 4-byte aligned.  B*H*N*d must stay below 2^40 elements.
+ *  - scale must be finite and > 0.
+ *  - Errors: argument problems return FA_ERR_INVALID_ARG or FA_ERR_UNSUPPORTED
+ *    before anything is launched; a failed launch returns FA_ERR_HIP.  No
+ *    exception or abort crosses the ABI.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element formats.  FA_FP8_E4M3 is OCP float8 e4m3fn (bias 7, no infinity,
+ * max finite 448), the format gfx950's matrix cores take. */
+typedef enum { FA_FP32 = 0, FA_BF16 = 1, FA_FP8_E4M3 = 2 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad scale, bad flag */
+  FA_ERR_UNSUPPORTED = 2, /* valid but not provided: d not in {64,128}, fp8 backward */
+  FA_ERR_HIP = 3          /* the HIP runtime rejected a launch */
+} fa_status;
+
+/* Forward pass ("FlashAttention-1: eliminating IO", sections 10.2.1-10.2.3;
+ * explainer V2 and V3 sections).
+ *   q, k, v : [B,H,N,d] inputs of type `dtype` (fp8: e4m3fn codes, 1 byte each)
+ *   o       : [B,H,N,d] output; float32 for FA_FP32, bfloat16 for FA_BF16 and
+ *             for FA_FP8_E4M3
+ *   lse     : [B,H,N] float32 output, ln sum_j exp(S_ij) over visible keys
+ *   scale   : multiplies Q K^T (1/sqrt(d) on the pages)
+ *   causal  : 0 or 1
+ *   q_descale, k_descale, v_descale : fp8 only -- the real value of a code c
+ *             is decode(c) * descale (one scale per tensor, finite, > 0);
+ *             ignored for the other formats.
+ * Accumulation is float32 for every format. */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, int dtype, float q_descale,
+                 float k_descale, float v_descale, void* stream);
+
+/* Bytes of device workspace fa_bwd needs for these sizes (delta, one float32
+ * per row, at the start of the workspace).  Returns 0 for invalid sizes. */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/* Backward pass ("FlashAttention-1: eliminating IO", section 10.2.4).
+ *   q, k, v, o, dout : [B,H,N,d] of type `dtype` (o as written by fa_fwd)
+ *   lse              : [B,H,N] float32 from fa_fwd
+ *   dq, dk, dv       : [B,H,N,d] outputs of type `dtype`
+ *   workspace        : device buffer of at least fa_bwd_workspace_size() bytes;
+ *                      on return its first B*H*N floats hold
+ *                      delta_i = sum_c dO_ic O_ic
+ *   workspace_bytes  : its size, checked
+ * dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO with dS = P o (dP - delta).
+ * Supported dtypes: FA_FP32 and FA_BF16 (FA_FP8_E4M3 -> FA_ERR_UNSUPPORTED). */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                 int dtype, void* stream);
+
+/* The three stages fa_bwd enqueues, in its order, with fa_bwd's arguments and
+ * validation (each stage uses the pointers it needs; the others must still be
+ * valid).  fa_bwd(...) is exactly fa_bwd_delta(...); fa_bwd_dkdv(...);
+ * fa_bwd_dq(...) on one stream.  They let a caller schedule or time the stages
+ * separately.
+ *   fa_bwd_delta : delta_i = dO_i . O_i into the workspace (FA1 page, 10.2.4)
+ *   fa_bwd_dkdv  : dK and dV, reading delta from the workspace
+ *   fa_bwd_dq    : dQ, reading delta from the workspace
+ * dkdv and dq need a delta written earlier on the same stream (or made
+ * visible by the caller's synchronisation). */
+fa_status fa_bwd_delta(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                       float scale, int causal, int dtype, void* stream);
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                      float scale, int causal, int dtype, void* stream);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                    size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                    int dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

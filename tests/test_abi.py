@@ -1,0 +1,109 @@
+"""The C-ABI library: it loads, exports what include/fa.h declares, and rejects
+bad arguments before launching anything (no GPU needed: every call here fails
+validation or has no work, so no HIP call is made)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+fa = pytest.importorskip("exact_io_aware_11_amd")
+lib = fa.lib
+
+OK, INVALID, UNSUPPORTED = fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED
+P = 0x10000  # a 16-byte aligned fake address; never dereferenced in these tests
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
+                                    "fa_bwd_workspace_size", "fa_fwd", "fa_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    raw = ctypes.CDLL(fa._lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert set(fa._lib.SIGNATURES) == set(declared_functions())
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, d=64, scale=0.125, causal=0,
+             dtype=fa.FA_BF16, qd=1.0, kd=1.0, vd=1.0, stream=None)
+    a.update(kw)
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                      a["scale"], a["causal"], a["dtype"], a["qd"], a["kd"], a["vd"], a["stream"])
+
+
+def bwd(fn="fa_bwd", **kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, wsb=1 << 20, B=1, H=1,
+             N=16, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return getattr(lib, fn)(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                      a["dv"], a["ws"], a["wsb"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                      a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(d=0), INVALID),
+    (dict(d=-64), INVALID), (dict(dtype=3), INVALID), (dict(dtype=-1), INVALID),
+    (dict(causal=2), INVALID), (dict(B=-1), INVALID), (dict(H=-2), INVALID),
+    (dict(N=-1), INVALID), (dict(scale=0.0), INVALID), (dict(scale=-0.1), INVALID),
+    (dict(scale=math.nan), INVALID), (dict(scale=math.inf), INVALID),
+    (dict(q=0), INVALID), (dict(k=0), INVALID), (dict(v=0), INVALID), (dict(o=0), INVALID),
+    (dict(lse=0), INVALID), (dict(q=P + 8), INVALID), (dict(o=P + 2), INVALID),
+    (dict(lse=P + 2), INVALID),
+    (dict(dtype=fa.FA_FP8_E4M3, qd=0.0), INVALID),
+    (dict(dtype=fa.FA_FP8_E4M3, vd=math.nan), INVALID),
+    (dict(B=1 << 20, H=1 << 20, N=1 << 20), INVALID),
+])
+def test_fwd_rejects_before_launch(kw, status):
+    assert fwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, q=0, k=0, v=0)])
+def test_fwd_empty_is_a_noop(kw):
+    assert fwd(**kw) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_FP8_E4M3), UNSUPPORTED), (dict(d=80), UNSUPPORTED),
+    (dict(dtype=9), INVALID), (dict(causal=-1), INVALID), (dict(scale=0.0), INVALID),
+    (dict(ws=0), INVALID), (dict(do=0), INVALID), (dict(dq=0), INVALID),
+    (dict(dk=P + 4), INVALID), (dict(ws=P + 2), INVALID), (dict(wsb=16), INVALID),
+])
+@pytest.mark.parametrize("fn", ["fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq"])
+def test_bwd_rejects_before_launch(kw, status, fn):
+    assert bwd(fn, **kw) == status
+
+
+def test_bwd_empty_is_a_noop():
+    assert bwd(N=0) == OK and bwd(B=0, q=0) == OK
+
+
+def test_workspace_size():
+    assert lib.fa_bwd_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 4
+    assert lib.fa_bwd_workspace_size(1, 1, 3, 64) == 256  # rounded up to 256 bytes
+    assert lib.fa_bwd_workspace_size(1, 1, 3, 96) == 0
+    assert lib.fa_bwd_workspace_size(-1, 1, 3, 64) == 0
+    assert fa.fa_bwd_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 4
+
+
+def test_status_strings():
+    for s in (0, 1, 2, 3, 99, -5):
+        assert isinstance(fa.fa_status_string(s), str) and fa.fa_status_string(s)
+    assert fa.fa_status_string(OK) == "ok"
+
+
+def test_flop_counts():
+    assert fa.flops_fwd(2, 32, 8192, 128, True) == 2 * 2 * 32 * 8192 ** 2 * 128
+    assert fa.flops_bwd(2, 16, 4096, 128, True) == 5 * 2 * 16 * 4096 ** 2 * 128

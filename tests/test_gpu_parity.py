@@ -1,0 +1,226 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle on
+the same seeded inputs (the oracle consumes the exact values the GPU gets).
+
+Bars: float32 -- max abs error <= 1e-5 on every output; bf16 -- max error
+<= 2e-2 * max|oracle| per tensor (O, dQ, dK, dV); fp8 -- 6e-2 * max|oracle|
+(O).  LSE (float32 in every format): |err| <= 1e-5 (fp32), 1e-3 + 1e-5|LSE|
+(bf16), 1e-2 + 1e-4|LSE| (fp8).  Outputs are prefilled with NaN, so an
+unwritten element fails.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs
+import oracle
+from _util import check, exact_values, run_bwd, run_fwd, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import exact_io_aware_11_amd as fa  # noqa: E402  (loads libfa.so; fails loudly if missing)
+
+
+def full_check_fwd(inp, scale, causal, tag):
+    say(f"{tag}: fwd {inp.dtype} shape={inp.q.shape} causal={causal}")
+    dev, o, lse = run_fwd(inp, scale, causal)
+    qs, ks, vs = (exact_values(x, inp.dtype, s) for x, s in zip((inp.q, inp.k, inp.v), inp.descale))
+    o_ref, lse_ref = oracle.attn_fwd(qs, ks, vs, scale, causal)
+    check(f"{tag} O", to_f64(o), o_ref, inp.dtype)
+    check(f"{tag} LSE", to_f64(lse), lse_ref, inp.dtype, lse=True)
+    return dev, o, lse, (qs, ks, vs)
+
+
+def full_check_bwd(inp, scale, causal, tag):
+    dev, o, lse, (qs, ks, vs) = full_check_fwd(inp, scale, causal, tag)
+    say(f"{tag}: bwd")
+    (dq, dk, dv), delta = run_bwd(dev, o, lse, inp, scale, causal)
+    dos = exact_values(inp.dout, inp.dtype)
+    rq, rk, rv = oracle.attn_bwd(qs, ks, vs, dos, scale, causal)
+    check(f"{tag} dQ", to_f64(dq), rq, inp.dtype)
+    check(f"{tag} dK", to_f64(dk), rk, inp.dtype)
+    check(f"{tag} dV", to_f64(dv), rv, inp.dtype)
+    # delta is computed from the O the GPU wrote: compare with that O exactly
+    d_ref = np.sum(to_f64(o) * dos, axis=-1)
+    e = float(np.max(np.abs(to_f64(delta) - d_ref)) / max(np.max(np.abs(d_ref)), 1e-30))
+    say(f"{tag} delta: rel err {e:.3e}")
+    assert e < 1e-5
+
+
+# --------------------------------------------------------------------------- #
+# float32 (the fp32 workload and ragged variants)
+# --------------------------------------------------------------------------- #
+def test_fp32_workload_fwd_bwd():
+    w = fa_inputs.WORKLOADS["fp32_fwdbwd_b1h1n128d64"]
+    inp = fa_inputs.make_inputs(w.shape, "fp32", seed=42)
+    full_check_bwd(inp, w.scale, w.causal, "fp32 b1h1n128d64")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 2, 1, 64, False), (2, 1, 33, 64, True), (1, 1, 100, 128, False), (1, 2, 100, 128, True),
+    (1, 1, 257, 64, True), (1, 1, 128, 64, True)])
+def test_fp32_shapes(B, H, N, d, causal):
+    inp = fa_inputs.make_inputs((B, H, N, d), "fp32", seed=N + d)
+    full_check_bwd(inp, 1 / math.sqrt(d), causal, f"fp32 {B}x{H}x{N}x{d}")
+
+
+# --------------------------------------------------------------------------- #
+# bf16 small shapes: several tiles, ragged tails, both masks, both head sizes
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("N", [1, 65, 257, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_fwd_bwd_small(N, d, causal):
+    inp = fa_inputs.make_inputs((2, 3, N, d), "bf16", seed=7 * N + d)
+    full_check_bwd(inp, 1 / math.sqrt(d), causal, f"bf16 2x3x{N}x{d}")
+
+
+@pytest.mark.parametrize("N", [1, 100, 513])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_fwd_small(N, d, causal):
+    inp = fa_inputs.make_inputs((1, 3, N, d), "fp8", seed=11 * N + d, with_dout=False)
+    full_check_fwd(inp, 1 / math.sqrt(d), causal, f"fp8 1x3x{N}x{d}")
+
+
+# --------------------------------------------------------------------------- #
+# The four large workloads at full size: sampled rows / heads against the oracle
+# --------------------------------------------------------------------------- #
+def sampled_fwd_check(w, heads, rows, seed=42):
+    inp = fa_inputs.make_inputs(w.shape, w.dtype, seed=seed, with_dout=False)
+    dev, o, lse = run_fwd(inp, w.scale, w.causal)
+    o_all, lse_all = to_f64(o), to_f64(lse)
+    assert np.isfinite(o_all).all() and np.isfinite(lse_all).all()
+    for (b, h) in heads:
+        qs, ks, vs = (exact_values(x[b, h], w.dtype, s)
+                      for x, s in zip((inp.q, inp.k, inp.v), inp.descale))
+        o_ref, lse_ref = oracle.attn_fwd_rows(qs, ks, vs, rows, w.scale, w.causal)
+        check(f"{w.name} head ({b},{h}) O rows", o_all[b, h, rows], o_ref, w.dtype)
+        check(f"{w.name} head ({b},{h}) LSE rows", lse_all[b, h, rows], lse_ref, w.dtype,
+              lse=True)
+    return inp, dev, o, lse
+
+
+def sample_rows(N, n=24, seed=0):
+    r = np.random.default_rng(seed).choice(N, size=n, replace=False)
+    edge = [0, 1, 31, 32, 63, 64, 127, 128, N // 2, N - 2, N - 1]
+    return np.unique(np.concatenate([r, edge]))
+
+
+def test_full_bf16_fwd_b4h16n2048d64():
+    w = fa_inputs.WORKLOADS["bf16_fwd_b4h16n2048d64"]
+    sampled_fwd_check(w, [(0, 0), (3, 15), (2, 7)], sample_rows(w.N))
+
+
+def test_full_bf16_causal_fwd_b2h32n8192d128():
+    w = fa_inputs.WORKLOADS["bf16_causal_fwd_b2h32n8192d128"]
+    sampled_fwd_check(w, [(0, 0), (1, 31), (0, 17)], sample_rows(w.N))
+
+
+def test_full_fp8_fwd_b1h32n16384d128():
+    w = fa_inputs.WORKLOADS["fp8_fwd_b1h32n16384d128"]
+    sampled_fwd_check(w, [(0, 0), (0, 31)], sample_rows(w.N, n=16))
+
+
+def test_full_bf16_causal_fwd_bwd_b2h16n4096d128():
+    w = fa_inputs.WORKLOADS["bf16_causal_fwdbwd_b2h16n4096d128"]
+    inp = fa_inputs.make_inputs(w.shape, w.dtype, seed=42)
+    rows = sample_rows(w.N)
+    dev, o, lse = run_fwd(inp, w.scale, w.causal)
+    (dq, dk, dv), _ = run_bwd(dev, o, lse, inp, w.scale, w.causal)
+    for name, t in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert torch.isfinite(t.float()).all(), name
+    for (b, h) in [(0, 0), (1, 15)]:
+        qs, ks, vs, dos = (exact_values(x[b, h], "bf16")
+                           for x in (inp.q, inp.k, inp.v, inp.dout))
+        o_ref, lse_ref = oracle.attn_fwd_rows(qs, ks, vs, rows, w.scale, w.causal)
+        check(f"{w.name} ({b},{h}) O rows", to_f64(o[b, h])[rows], o_ref, "bf16")
+        check(f"{w.name} ({b},{h}) LSE rows", to_f64(lse[b, h])[rows], lse_ref, "bf16", lse=True)
+        say(f"{w.name} ({b},{h}): oracle backward for the whole head")
+        rq, rk, rv = oracle.attn_bwd(qs[None, None], ks[None, None], vs[None, None],
+                                     dos[None, None], w.scale, w.causal)
+        check(f"{w.name} ({b},{h}) dQ", to_f64(dq[b, h]), rq[0, 0], "bf16")
+        check(f"{w.name} ({b},{h}) dK", to_f64(dk[b, h]), rk[0, 0], "bf16")
+        check(f"{w.name} ({b},{h}) dV", to_f64(dv[b, h]), rv[0, 0], "bf16")
+
+
+# --------------------------------------------------------------------------- #
+# Edge cases and special inputs
+# --------------------------------------------------------------------------- #
+def bf16_inputs_from(q, k, v, do=None):
+    return fa_inputs.Inputs(fa_inputs.to_bf16_bits(q), fa_inputs.to_bf16_bits(k),
+                            fa_inputs.to_bf16_bits(v),
+                            None if do is None else fa_inputs.to_bf16_bits(do), (1., 1., 1.),
+                            "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_queries_average_values(causal):
+    q, k, v, do = fa_inputs.draw_f32((1, 2, 300, 128), seed=5)
+    inp = bf16_inputs_from(np.zeros_like(q), k, v, do)
+    full_check_bwd(inp, 1 / math.sqrt(128), causal, "bf16 zero Q")
+
+
+def test_constant_values_return_values():
+    """Rows of P sum to one: a constant V comes back to within one bf16 step."""
+    q, k, v, _ = fa_inputs.draw_f32((1, 1, 333, 64), seed=6)
+    v[:] = v[:, :, :1, :]
+    inp = bf16_inputs_from(q, k, v)
+    _, o, _ = run_fwd(inp, 0.125, False)
+    ref = exact_values(inp.v, "bf16")
+    assert np.all(np.abs(to_f64(o) - ref) <= 2.0 ** -7 * np.abs(ref))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp8"])
+def test_causal_first_row_is_v0(dtype):
+    inp = fa_inputs.make_inputs((2, 2, 200, 128), dtype, seed=8, with_dout=False)
+    _, o, lse = run_fwd(inp, 1 / math.sqrt(128), True)
+    v0 = exact_values(inp.v[:, :, 0], dtype, inp.descale[2])
+    if dtype == "fp8":  # O is bf16: V_0 times v_descale rounded once
+        v0 = to_f64(torch.from_numpy(v0).float().to(torch.bfloat16))
+    np.testing.assert_array_equal(to_f64(o[:, :, 0]), v0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_magnitude_scores(causal):
+    q, k, v, do = fa_inputs.draw_f32((1, 2, 256, 128), seed=9)
+    inp = bf16_inputs_from(50 * q, k, v, do)
+    full_check_bwd(inp, 1 / math.sqrt(128), causal, "bf16 50x Q")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_runs_are_bitwise_deterministic(dtype):
+    inp = fa_inputs.make_inputs((2, 4, 700, 128), dtype, seed=10)
+    dev, o1, l1 = run_fwd(inp, 0.088, True)
+    (a1, b1, c1), _ = run_bwd(dev, o1, l1, inp, 0.088, True)
+    _, o2, l2 = run_fwd(inp, 0.088, True)
+    (a2, b2, c2), _ = run_bwd(dev, o2, l2, inp, 0.088, True)
+    for x, y in ((o1, o2), (l1, l2), (a1, a2), (b1, b2), (c1, c2)):
+        assert torch.equal(x, y)
+
+
+def test_empty_problem_is_a_noop():
+    z = torch.empty((2, 3, 0, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((2, 3, 0), dtype=torch.float32, device="cuda")
+    fa.fa_fwd(z, z, z, z, lse, 0.125, True)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    fa.fa_bwd(z, z, z, z, z, lse, z, z, z, ws, 0.125, True)
+    torch.cuda.synchronize()
+
+
+def test_bad_arguments_raise_without_launch():
+    x = torch.zeros((1, 1, 8, 96), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((1, 1, 8), dtype=torch.float32, device="cuda")
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_fwd(x, x, x, x, lse, 0.1, False)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+    y = torch.zeros((1, 1, 8, 64), dtype=torch.uint8, device="cuda")
+    l8 = torch.zeros((1, 1, 8), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_bwd(y, y, y, y, y, l8, y, y, y, ws, 0.1, False)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
