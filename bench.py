@@ -35,6 +35,35 @@ MAIN = "bf16_causal_fwdbwd_b2h16n4096d128"
 EXTRA = ["bf16_causal_fwd_b2h32n8192d128", "bf16_fwd_b4h16n2048d64", "fp8_fwd_b1h32n16384d128"]
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources (name + bytes, sorted by name)."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "exact_io_aware_11_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a copy-kernel calibration),
+    or None if it was taken on other kernel sources or another workload."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    st = t.get("stages", {}).get(stage)
+    return None if st is None else st["bytes_per_launch"]
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -184,6 +213,27 @@ def cpu_baseline(w, max_heads):
                       f"({'fwd+bwd' if w.backward else 'fwd'}), float64 naive oracle"}
 
 
+def calibrate_copy(nbytes: int = 1 << 30, reps: int = 3):
+    """A plain device-to-device copy of known size: each launch reads and
+    writes nbytes.  Profiling it with the HBM byte counters gives the factor
+    that turns counter readings into bytes."""
+    import torch
+
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps,
+                      "ms": round(ms, 4), "GB/s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +243,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--hbm-calibrate", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: every (batch, head) is independent, so "
@@ -201,6 +253,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.hbm_calibrate:
+        calibrate_copy()
+        return
 
     import exact_io_aware_11_amd as fa  # noqa: F401  (fails loudly without libfa.so)
     import fa_inputs
@@ -229,7 +285,7 @@ def main():
         ach = work[dom] / (per[dom] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name, dom)
     value = total_flops / (ms * 1e-3) / 1e12
     log(f"step {ms:.3f} ms  {value:.1f} TFLOP/s  kernels {kernels}")
 
