@@ -29,6 +29,9 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// The forward moves its reference row max only when a score exceeds it by
+// more than this many powers of two (probabilities stay <= 2^16).
+constexpr float kRescaleLog2 = 16.f;
 
 __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -102,12 +105,21 @@ __device__ __forceinline__ void map_block(uint32_t w, uint32_t n_blk, uint32_t t
   if (heavy_first_reverse) blk = n_blk - 1u - blk;
 }
 
-// 16-byte-chunk XOR swizzle of a [rows][D] bf16 tile in LDS.  Lanes that read
-// the same logical chunk of 16 consecutive rows hit 16 different bank groups.
+// 16-byte-chunk XOR swizzle of a [rows][D] bf16 tile in LDS (D = 64 or 128).
+// It serves the two read patterns the kernels use, both free of bank
+// conflicts (64 banks x 4 bytes):
+//  * ds_read_b128 of one logical chunk by 16 consecutive rows (A/B operands
+//    along the head dimension): the 16 rows land in 16 different 16-byte
+//    bank groups;
+//  * ds_read_b64_tr_b16 of 4 consecutive logical chunks by 4 consecutive
+//    rows (the transposed operand): the 16 (row, chunk) pairs land in 16
+//    different bank groups.
+// Rows are 256 bytes (D = 128, one full bank sweep) or 128 bytes (D = 64,
+// two rows per sweep); the swizzle depends only on row % 16.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return row & 15;
-  else return (row >> 1) & 7;
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int chunk) {  // element offset

@@ -25,6 +25,8 @@
 //  * K and V tiles are double-buffered in LDS (16-byte XOR swizzle), staged
 //    from HBM with 16-byte loads issued one tile ahead; one barrier per tile.
 //  * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -34,10 +36,11 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int N,
-    uint32_t n_qblk, uint32_t total, float scale, float scale_log2) {
-  constexpr int BM = 128, BN = 64, CH = D / 8, TILE = BN * D;
-  constexpr int PER = BN * CH / 256;  // 16-byte chunks per thread per tensor per tile
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [buffer][K, V]
+    uint32_t n_qblk, uint32_t total, float scale, float scale_log2, float grow_thr) {
+  constexpr int BM = 128, BN = 64, TILE = BN * D;  // TILE: elements of one K or V tile
+  constexpr int LPW = TILE * 2 / 1024 / 4;         // 1 KiB direct loads per wave per tile
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[2][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
@@ -62,119 +65,204 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int kv_end = CAUSAL ? min(N, (int)qblk * BM + BM) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
 
-  uint4 kreg[PER], vreg[PER];
-  auto gload = [&](int j) {
+  // Per-lane element offsets inside one tile buffer (the swizzle depends only
+  // on row % 16, so whole 16-row steps are plain constants added to these).
+  int koff[D / 16];  // K as the A operand: row r32 (+32b), chunk 2t + g
 #pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      const int c = tid + 256 * x, row = c / CH, ch = c % CH, key = j * BN + row;
-      if (key < N) {
-        kreg[x] = *reinterpret_cast<const uint4*>(Kh + (size_t)key * D + ch * 8);
-        vreg[x] = *reinterpret_cast<const uint4*>(Vh + (size_t)key * D + ch * 8);
-      } else {
-        kreg[x] = make_uint4(0, 0, 0, 0);
-        vreg[x] = make_uint4(0, 0, 0, 0);
-      }
+  for (int t = 0; t < D / 16; ++t) koff[t] = tile_off<D>(r32, 2 * t + g);
+  // V by the transposing read: source lane (r, c) = ((lane%16)/4, lane%4) reads
+  // row 4g + r (+8 for keys 8..15 of a 16-key step) at head dim 32cb + 16((lane/16)%2) + 4c.
+  const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_n0 = 16 * ((lane >> 4) & 1);
+  int voff[D / 32][2];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) {
+    const int d = 32 * cb + tr_n0 + 4 * tr_c;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) voff[cb][hf] = tile_off<D>(4 * g + tr_r + 8 * hf, d >> 3) + (d & 7);
+  }
+  // Direct HBM -> LDS staging: load x of this wave fills bytes
+  // [(wave*LPW + x) * 1024, +1024) of a tile buffer, lane l the 16 bytes at
+  // +16 l.  Those bytes are physical chunk (16 l % 2D)/16 of tile row
+  // (byte / 2D); the lane therefore fetches the logical chunk that the
+  // swizzle puts there.
+  int grow[LPW], gcol[LPW];
+#pragma unroll
+  for (int x = 0; x < LPW; ++x) {
+    const int byte = (wave * LPW + x) * 1024 + 16 * lane;
+    grow[x] = byte / (2 * D);
+    gcol[x] = (((byte % (2 * D)) >> 4) ^ swz<D>(grow[x])) << 3;
+  }
+  // Rows past N are fetched from row N - 1 instead (finite data; those keys
+  // are masked, so their scores never count and their P is exactly 0).
+  auto stage = [&](const uint16_t* src, uint16_t* dst, int key0) {
+#pragma unroll
+    for (int x = 0; x < LPW; ++x) {
+      const int row = min(key0 + grow[x], N - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src + (size_t)row * D + gcol[x]),
+          (__attribute__((address_space(3))) void*)(dst + (wave * LPW + x) * 512), 16, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      const int c = tid + 256 * x, row = c / CH, ch = c % CH;
-      *reinterpret_cast<uint4*>(&lds[buf][0][tile_off<D>(row, ch)]) = kreg[x];
-      *reinterpret_cast<uint4*>(&lds[buf][1][tile_off<D>(row, ch)]) = vreg[x];
-    }
-  };
-
-  // Per-lane source address pieces of the transposing V read.
-  const int tr_src = lane & 15, tr_r = tr_src >> 2, tr_c = tr_src & 3;
-  const int tr_n0 = 16 * ((lane >> 4) & 1);
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  auto active = [&](int j) { return !CAUSAL || j * BN <= q0 + 31; };
+  auto scores = [&](const uint16_t* Kt, f32x16& s0, f32x16& s1) {
+    s0 = mfma_bf16(lds_read_b128(Kt + koff[0]), qf[0], f32x16{});
+    s1 = mfma_bf16(lds_read_b128(Kt + 32 * D + koff[0]), qf[0], f32x16{});
+#pragma unroll
+    for (int t = 1; t < D / 16; ++t) {
+      s0 = mfma_bf16(lds_read_b128(Kt + koff[t]), qf[t], s0);
+      s1 = mfma_bf16(lds_read_b128(Kt + 32 * D + koff[t]), qf[t], s1);
+    }
+  };
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) gload(j + 1);
-    const int key0 = j * BN;
-    const bool active = !CAUSAL || key0 <= q0 + 31;
-    if (active) {
-      const uint16_t* Kt = lds[buf][0];
-      const uint16_t* Vt = lds[buf][1];
-      f32x16 s[2];
+  // Online softmax of tile j's scores, then O^T += V_j^T P_j^T.
+  // O^T += V_j^T P_j^T with P_j in bf16 (the B operand exactly as the
+  // accumulator layout left it; V read transposed in the same key order).
+  auto pv = [&](const uint16_t* Vt, bf16x8 p00, bf16x8 p01, bf16x8 p10, bf16x8 p11) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        s[b] = f32x16{};
-        const int krow = 32 * b + r32;
+    for (int cb = 0; cb < D / 32; ++cb) {
+      const uint16_t* vb = Vt + voff[cb][0];
+      const uint16_t* vc = Vt + voff[cb][1];
+      acc[cb] = mfma_bf16(concat(lds_read_tr16(vb), lds_read_tr16(vc)), p00, acc[cb]);
+      acc[cb] = mfma_bf16(concat(lds_read_tr16(vb + 16 * D), lds_read_tr16(vc + 16 * D)), p01, acc[cb]);
+      acc[cb] = mfma_bf16(concat(lds_read_tr16(vb + 32 * D), lds_read_tr16(vc + 32 * D)), p10, acc[cb]);
+      acc[cb] = mfma_bf16(concat(lds_read_tr16(vb + 48 * D), lds_read_tr16(vc + 48 * D)), p11, acc[cb]);
+    }
+  };
+
+  // Online softmax (FA1 page 10.2.2; reading notes code 3-1) against a
+  // running reference max m_run.  Lazy rescale: m_run only moves when some
+  // row's tile max exceeds it by more than grow_thr (2^16 in probability);
+  // the accumulator and row sum are then rescaled by alpha = exp(m_old -
+  // m_new).  Otherwise the probabilities exp(S - m_run) may reach 2^16,
+  // which float32 accumulation and bf16 P hold exactly as well as values <= 1
+  // -- any reference gives the same exact result.  The first tile always
+  // moves m_run off -infinity.
+  auto rowmax_guard = [&](const f32x16& s0, const f32x16& s1) {
+    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t)
-          s[b] = mfma_bf16(lds_read_b128(Kt + tile_off<D>(krow, 2 * t + g)), qf[t], s[b]);
-      }
-      const bool need_mask = (key0 + BN > N) || (CAUSAL && key0 + BN - 1 > q0);
-      if (need_mask) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= N || (CAUSAL && key > qrow)) s[b][i] = -INFINITY;
-          }
-      }
-      float mx = s[0][0];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
-      mx = halves_max(mx);
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    mx = halves_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + grow_thr) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2_fast((m_run - m_new) * scale_log2);
-      const float mneg = -m_new * scale_log2;
-      // The row sum is taken over the float32 probabilities (so LSE carries
-      // no bf16 rounding); P rounded to bf16 feeds the P V product.
-      float rs = 0.f;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[b][i] = exp2_fast(fmaf(s[b][i], scale_log2, mneg));
-          rs += s[b][i];
-        }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
-
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) pf[b][h] = to_bf16x8(s[b], 8 * h);
-
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-        const int d = 32 * cb + tr_n0 + 4 * tr_c;
-        const int ch = d >> 3, sub = d & 7;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int kr0 = 32 * b + 16 * h + 4 * g + tr_r;
-            const int kr1 = kr0 + 8;
-            const bf16x4 lo = lds_read_tr16(Vt + tile_off<D>(kr0, ch) + sub);
-            const bf16x4 hi = lds_read_tr16(Vt + tile_off<D>(kr1, ch) + sub);
-            acc[cb] = mfma_bf16(concat(lo, hi), pf[b][h], acc[cb]);
-          }
-      }
+      m_run = m_new;
     }
-    if (j + 1 < n_tiles) lstore(buf ^ 1);
+  };
+  // P = exp(S - m_run) in place; row sum over the float32 P; P in bf16 out.
+  auto exps = [&](f32x16& s0, f32x16& s1, bf16x8& p00, bf16x8& p01, bf16x8& p10,
+                  bf16x8& p11) {
+    const float mneg = -m_run * scale_log2;
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = exp2_fast(fmaf(s0[i], scale_log2, mneg));
+      s1[i] = exp2_fast(fmaf(s1[i], scale_log2, mneg));
+      rs0 += s0[i];
+      rs1 += s1[i];
+    }
+    l_run += rs0 + rs1;
+    p00 = to_bf16x8(s0, 0);
+    p01 = to_bf16x8(s0, 8);
+    p10 = to_bf16x8(s1, 0);
+    p11 = to_bf16x8(s1, 8);
+  };
+
+  // Masked scores: keys past N, and under the causal mask keys after the query.
+  auto apply_mask = [&](f32x16& s0, f32x16& s1, int key0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = key0 + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (key >= N || (CAUSAL && key > qrow)) s0[i] = -INFINITY;
+      if (key + 32 >= N || (CAUSAL && key + 32 > qrow)) s1[i] = -INFINITY;
+    }
+  };
+
+  // Software pipeline: K runs one tile ahead of V.  At step j the LDS holds
+  // K_{j+1} and V_j; S_{j+1} = K_{j+1} Q^T is issued to the matrix cores
+  // interleaved with the softmax of tile j; then P_j V_j.  K_{j+2} and
+  // V_{j+1} stream in meanwhile.  One barrier per step.  Tiles
+  // [0, j_full) need no mask for any row of the workgroup and are not the
+  // last tile; the causal diagonal tiles, a ragged tail and the last tile
+  // take the general step.
+  const int j_full = min(min(CAUSAL ? (int)qblk * (BM / BN) : n_tiles, N / BN), n_tiles - 1);
+  f32x16 sc0, sc1, sn0, sn1;
+  stage(Kh, lds_k[0], 0);
+  stage(Vh, lds_v[0], 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (n_tiles > 1) stage(Kh, lds_k[1], BN);
+  if (active(0)) scores(lds_k[0], sc0, sc1);
+
+  auto step_full = [&](auto parity, int j) {
+    constexpr int P = decltype(parity)::value;  // j % 2
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces of K_{j+1} and V_j have landed
+    __syncthreads();                 // ... and everyone's
+    if (j + 1 < n_tiles) stage(Vh, lds_v[P ^ 1], (j + 1) * BN);
+    if (j + 2 < n_tiles) stage(Kh, lds_k[P], (j + 2) * BN);
+    bf16x8 p00, p01, p10, p11;
+    rowmax_guard(sc0, sc1);
+    // j + 1 < n_tiles holds (the last tile is never a full step) and every
+    // wave is active on full tiles.
+    scores(lds_k[P ^ 1], sn0, sn1);
+    exps(sc0, sc1, p00, p01, p10, p11);
+    // interleave: per S MFMA, one K read and a share of the softmax VALU
+#pragma unroll
+    for (int i = 0; i < 2 * (D / 16); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    pv(lds_v[P], p00, p01, p10, p11);
+    sc0 = sn0;
+    sc1 = sn1;
+  };
+  auto step_masked = [&](auto parity, int j) {
+    constexpr int P = decltype(parity)::value;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (j + 1 < n_tiles) stage(Vh, lds_v[P ^ 1], (j + 1) * BN);
+    if (j + 2 < n_tiles) stage(Kh, lds_k[P], (j + 2) * BN);
+    const bool nxt = j + 1 < n_tiles && active(j + 1);
+    if (nxt) scores(lds_k[P ^ 1], sn0, sn1);
+    if (active(j)) {
+      bf16x8 p00, p01, p10, p11;
+      apply_mask(sc0, sc1, j * BN);
+      rowmax_guard(sc0, sc1);
+      exps(sc0, sc1, p00, p01, p10, p11);
+      pv(lds_v[P], p00, p01, p10, p11);
+    }
+    if (nxt) {
+      sc0 = sn0;
+      sc1 = sn1;
+    }
+  };
+  int j = 0;
+  for (; j + 1 < j_full; j += 2) {
+    step_full(std::integral_constant<int, 0>{}, j);
+    step_full(std::integral_constant<int, 1>{}, j + 1);
+  }
+  if (j < j_full) {
+    step_full(std::integral_constant<int, 0>{}, j);
+    ++j;
+    if (j < n_tiles) {
+      step_masked(std::integral_constant<int, 1>{}, j);
+      ++j;
+    }
+  }
+  for (; j < n_tiles; j += 2) {
+    step_masked(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_tiles) step_masked(std::integral_constant<int, 1>{}, j + 1);
   }
 
   const float l_tot = halves_sum(l_run);
@@ -200,7 +288,8 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   const uint32_t total = (uint32_t)(a.BH * n_qblk);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.N, n_qblk, total, a.scale, a.scale * kLog2e);
+                     (uint16_t*)a.o, a.lse, a.N, n_qblk, total, a.scale, a.scale * kLog2e,
+                     kRescaleLog2 / (a.scale * kLog2e));
   return hipGetLastError();
 }
 
