@@ -22,6 +22,8 @@
 //    the transposing LDS read.
 // Recomputing S and dP in the dQ pass costs two extra matrix products over
 // the five the method needs; it keeps every output written exactly once.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -34,10 +36,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int N, uint32_t n_kblk, uint32_t total, float scale,
     float scale_log2) {
-  constexpr int BN = 128, BM = 64, CH = D / 8, TILE = BM * D;
-  constexpr int PER = BM * CH / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];      // [buffer][LSE*log2e, delta]
+  constexpr int BN = 128, BM = 64, TILE = BM * D;
+  constexpr int LPW = TILE * 2 / 1024 / 4;  // 1 KiB direct loads per wave per tile
+  constexpr int NT = D / 16, NCB = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint16_t lq[2][TILE];   // Q tiles
+  __shared__ __attribute__((aligned(1024))) uint16_t lo[2][TILE];   // dO tiles
+  __shared__ __attribute__((aligned(16))) float lst[2][2][BM];      // [buffer][LSE*log2e, delta]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
@@ -53,9 +57,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const int kcol = k0 + r32;  // this lane's key (C-layout column)
 
   // K and V rows as the B operands of S = Q K^T and dP = dO V^T.
-  bf16x8 kf[D / 16], vf[D / 16];
+  bf16x8 kf[NT], vf[NT];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
+  for (int t = 0; t < NT; ++t) {
     if (kcol < N) {
       kf[t] = *reinterpret_cast<const bf16x8*>(K + head + (size_t)kcol * D + 16 * t + 8 * g);
       vf[t] = *reinterpret_cast<const bf16x8*>(V + head + (size_t)kcol * D + 16 * t + 8 * g);
@@ -65,122 +69,196 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     }
   }
 
+  // Per-lane LDS element offsets (the swizzle depends only on row % 16).
+  int aoff[NT];  // Q / dO rows as A operands: row r32 (+32 qb), chunk 2t + g
+#pragma unroll
+  for (int t = 0; t < NT; ++t) aoff[t] = tile_off<D>(r32, 2 * t + g);
+  // Q^T / dO^T by the transposing read: row 4g + r (+8) (+16h +32qb), head dim
+  // 32cb + 16((lane/16)%2) + 4c for source lane (r, c) = ((lane%16)/4, lane%4).
+  const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_n0 = 16 * ((lane >> 4) & 1);
+  int toff[NCB][2];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int d = 32 * cb + tr_n0 + 4 * tr_c;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) toff[cb][hf] = tile_off<D>(4 * g + tr_r + 8 * hf, d >> 3) + (d & 7);
+  }
+  // Direct HBM -> LDS staging of Q and dO tiles (see the forward kernel).
+  int grow[LPW], gcol[LPW];
+#pragma unroll
+  for (int x = 0; x < LPW; ++x) {
+    const int byte = (wave * LPW + x) * 1024 + 16 * lane;
+    grow[x] = byte / (2 * D);
+    gcol[x] = (((byte % (2 * D)) >> 4) ^ swz<D>(grow[x])) << 3;
+  }
   const int n_it = (N + BM - 1) / BM;
   const int it0 = CAUSAL ? ((int)kblk * BN) / BM : 0;
-
-  uint4 qreg[PER], oreg[PER];
-  float sreg = 0.f;
-  auto gload = [&](int it) {
+  auto stage = [&](int it, int buf) {  // rows past N read row N - 1 (masked)
 #pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      const int c = tid + 256 * x, row = c / CH, ch = c % CH, q = it * BM + row;
-      if (q < N) {
-        qreg[x] = *reinterpret_cast<const uint4*>(Qh + (size_t)q * D + ch * 8);
-        oreg[x] = *reinterpret_cast<const uint4*>(dOh + (size_t)q * D + ch * 8);
-      } else {
-        qreg[x] = make_uint4(0, 0, 0, 0);
-        oreg[x] = make_uint4(0, 0, 0, 0);
-      }
+    for (int x = 0; x < LPW; ++x) {
+      const int row = min(it * BM + grow[x], N - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(Qh + (size_t)row * D + gcol[x]),
+          (__attribute__((address_space(3))) void*)(lq[buf] + (wave * LPW + x) * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(dOh + (size_t)row * D + gcol[x]),
+          (__attribute__((address_space(3))) void*)(lo[buf] + (wave * LPW + x) * 512), 16, 0, 0);
     }
+  };
+  float sreg = 0.f;  // threads 0..127 carry one LSE*log2e (0..63) or delta (64..127)
+  auto load_stats = [&](int it) {
     if (tid < 2 * BM) {
       const int q = it * BM + (tid & (BM - 1));
       sreg = q < N ? (tid < BM ? LSEh[q] * kLog2e : Dh[q]) : 0.f;
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      const int c = tid + 256 * x, row = c / CH, ch = c % CH;
-      *reinterpret_cast<uint4*>(&lds[buf][0][tile_off<D>(row, ch)]) = qreg[x];
-      *reinterpret_cast<uint4*>(&lds[buf][1][tile_off<D>(row, ch)]) = oreg[x];
-    }
-    if (tid < 2 * BM) stat[buf][tid / BM][tid & (BM - 1)] = sreg;
+  auto store_stats = [&](int buf) {
+    if (tid < 2 * BM) lst[buf][tid / BM][tid & (BM - 1)] = sreg;
   };
 
-  const int tr_src = lane & 15, tr_r = tr_src >> 2, tr_c = tr_src & 3;
-  const int tr_n0 = 16 * ((lane >> 4) & 1);
-
-  f32x16 adk[D / 32], adv[D / 32];
+  f32x16 adk[NCB], adv[NCB];
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
     adk[cb] = f32x16{};
     adv[cb] = f32x16{};
   }
 
-  if (it0 < n_it) {
-    gload(it0);
-    lstore(0);
-  }
-  __syncthreads();
+  // One 32-query half qb of a 64-query tile:
+  //  G_A(qb): S = Q_qb K^T and dP = dO_qb V^T (2 NT products, A from LDS rows)
+  //  SOFT(qb): P = exp2(S log2e scale - LSE log2e), dS = P (dP - delta)
+  //  G_B(qb): dV^T += dO_qb^T P and dK^T += Q_qb^T dS (4 NCB products, A by
+  //           the transposing read, B = P / dS straight from the C layout)
+  // Per tile: G_A(0); [G_A(1) | SOFT(0)]; [G_B(0) | SOFT(1)]; G_B(1), with
+  // the softmax arithmetic of one half interleaved, element by element, into
+  // the other half's products, and every operand fetched from LDS several
+  // products ahead (sched_barrier keeps that order).
+  f32x16 s[2], dp[2];
+  bf16x8 pb[2][2], db[2][2];
 
-  for (int it = it0; it < n_it; ++it) {
-    const int buf = (it - it0) & 1;
-    if (it + 1 < n_it) gload(it + 1);
+  auto tile = [&](auto bufc, int it, bool masked) {
+    constexpr int BUF = decltype(bufc)::value;
+    const uint16_t* Qt = lq[BUF];
+    const uint16_t* Ot = lo[BUF];
     const int qbase = it * BM;
-    const bool active = !CAUSAL || qbase + BM - 1 >= k0;
-    if (active) {
-      const uint16_t* Qt = lds[buf][0];
-      const uint16_t* Ot = lds[buf][1];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-        const int arow = 32 * qb + r32;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          s = mfma_bf16(lds_read_b128(Qt + tile_off<D>(arow, 2 * t + g)), kf[t], s);
-          dp = mfma_bf16(lds_read_b128(Ot + tile_off<D>(arow, 2 * t + g)), vf[t], dp);
-        }
-        const int qrow0 = qbase + 32 * qb;
-        const bool need_mask = (qrow0 + 32 > N) || (k0 + 32 > N) || (CAUSAL && k0 + 31 > qrow0);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int rr = 32 * qb + 8 * q4 + 4 * g;
-          const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stat[buf][0][rr]);
-          const f32x4 dl = *reinterpret_cast<const f32x4*>(&stat[buf][1][rr]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * q4 + e;
-            float p = exp2_fast(fmaf(s[i], scale_log2, -l2[e]));
-            if (need_mask) {
-              const int q = qbase + rr + e;
-              if (q >= N || kcol >= N || (CAUSAL && kcol > q)) p = 0.f;
-            }
-            s[i] = p;
-            dp[i] = p * (dp[i] - dl[e]);
-          }
-        }
-        bf16x8 pb[2], db[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          pb[h] = to_bf16x8(s, 8 * h);
-          db[h] = to_bf16x8(dp, 8 * h);
-        }
-#pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb) {
-          const int d = 32 * cb + tr_n0 + 4 * tr_c;
-          const int ch = d >> 3, sub = d & 7;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int r0 = 32 * qb + 16 * h + 4 * g + tr_r, r1 = r0 + 8;
-            const bf16x8 ao = concat(lds_read_tr16(Ot + tile_off<D>(r0, ch) + sub),
-                                     lds_read_tr16(Ot + tile_off<D>(r1, ch) + sub));
-            adv[cb] = mfma_bf16(ao, pb[h], adv[cb]);
-            const bf16x8 aq = concat(lds_read_tr16(Qt + tile_off<D>(r0, ch) + sub),
-                                     lds_read_tr16(Qt + tile_off<D>(r1, ch) + sub));
-            adk[cb] = mfma_bf16(aq, db[h], adk[cb]);
-          }
-        }
+    constexpr int NA = 2 * NT, NB = 4 * NCB, DEPTH = 6;
+    // operand fetches
+    auto fetch_a = [&](int qb, int k) -> bf16x8 {  // k-th product of G_A(qb)
+      const uint16_t* base = (k & 1) ? Ot : Qt;
+      return lds_read_b128(base + 32 * qb * D + aoff[k >> 1]);
+    };
+    auto fetch_b = [&](int qb, int k) -> bf16x8 {  // k-th product of G_B(qb)
+      const int h = k / (2 * NCB), cb = (k >> 1) % NCB;
+      const uint16_t* base = ((k & 1) ? Qt : Ot) + (32 * qb + 16 * h) * D;
+      return concat(lds_read_tr16(base + toff[cb][0]), lds_read_tr16(base + toff[cb][1]));
+    };
+    auto op_a = [&](int qb, int k, const bf16x8& a) {
+      if (k < 2) {
+        if (k == 0) s[qb] = mfma_bf16(a, kf[0], f32x16{});
+        else dp[qb] = mfma_bf16(a, vf[0], f32x16{});
+      } else if (k & 1) {
+        dp[qb] = mfma_bf16(a, vf[k >> 1], dp[qb]);
+      } else {
+        s[qb] = mfma_bf16(a, kf[k >> 1], s[qb]);
       }
+    };
+    auto op_b = [&](int qb, int k, const bf16x8& a) {
+      const int h = k / (2 * NCB), cb = (k >> 1) % NCB;
+      if (k & 1) adk[cb] = mfma_bf16(a, db[qb][h], adk[cb]);
+      else adv[cb] = mfma_bf16(a, pb[qb][h], adv[cb]);
+    };
+    // LSE*log2e and delta of the 16 rows a lane sees in half qb, read once
+    f32x4 l2v[4], dlv[4];
+    auto load_half_stats = [&](int qb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        l2v[q4] = *reinterpret_cast<const f32x4*>(&lst[BUF][0][32 * qb + 8 * q4 + 4 * g]);
+        dlv[q4] = *reinterpret_cast<const f32x4*>(&lst[BUF][1][32 * qb + 8 * q4 + 4 * g]);
+      }
+    };
+    // softmax-backward arithmetic of element i (0..15) of half qb
+    auto soft_elem = [&](int qb, int i) {
+      const int rr = 32 * qb + 8 * (i >> 2) + 4 * g + (i & 3);
+      const float l2 = l2v[i >> 2][i & 3], dl = dlv[i >> 2][i & 3];
+      float p = exp2_fast(fmaf(s[qb][i], scale_log2, -l2));
+      if (masked) {
+        const int q = qbase + rr;
+        if (q >= N || kcol >= N || (CAUSAL && kcol > q)) p = 0.f;
+      }
+      s[qb][i] = p;
+      dp[qb][i] = p * (dp[qb][i] - dl);
+      if ((i & 7) == 7) {
+        pb[qb][i >> 3] = to_bf16x8(s[qb], i - 7);
+        db[qb][i >> 3] = to_bf16x8(dp[qb], i - 7);
+      }
+    };
+    // A fenced stream of NOPS products of group (kind, qb) with operands
+    // fetched DEPTH ahead; `extra(k)` is softmax work woven in after product k.
+    auto stream = [&](bool kind_b, int qb, int nops, auto extra) {
+      bf16x8 ring[DEPTH + 1];
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k) ring[k] = kind_b ? fetch_b(qb, k) : fetch_a(qb, k);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < nops; ++k) {
+        if (k + DEPTH < nops)
+          ring[(k + DEPTH) % (DEPTH + 1)] = kind_b ? fetch_b(qb, k + DEPTH) : fetch_a(qb, k + DEPTH);
+        if (kind_b) op_b(qb, k, ring[k % (DEPTH + 1)]);
+        else op_a(qb, k, ring[k % (DEPTH + 1)]);
+        extra(k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto none = [](int) {};
+    load_half_stats(0);
+    stream(false, 0, NA, none);
+    // the 16 softmax elements of a half are spread evenly over a stream
+    stream(false, 1, NA, [&](int k) {
+#pragma unroll
+      for (int i = k * 16 / NA; i < (k + 1) * 16 / NA; ++i) soft_elem(0, i);
+    });
+    load_half_stats(1);
+    stream(true, 0, NB, [&](int k) {
+#pragma unroll
+      for (int i = k * 16 / NB; i < (k + 1) * 16 / NB; ++i) soft_elem(1, i);
+    });
+    stream(true, 1, NB, none);
+  };
+
+  // Two-stage pipeline over query tiles: tile it+1 streams into the other
+  // buffer while tile it is processed; one barrier per tile.  The barrier
+  // waits only for this wave's loads of the tile about to be used.
+  auto step = [&](auto bufc, int it) {
+    constexpr int BUF = decltype(bufc)::value;
+    barrier_vm<0>();  // tile `it` (loads of the previous step) visible to all
+    const bool more = it + 1 < n_it;
+    if (more) {
+      stage(it + 1, BUF ^ 1);
+      load_stats(it + 1);
     }
-    if (it + 1 < n_it) lstore(buf ^ 1);
-    __syncthreads();
+    const int qbase = it * BM;
+    const bool wave_active = !CAUSAL || qbase + BM - 1 >= k0;
+    if (wave_active) {
+      const bool masked = (qbase + BM > N) || (k0 + 32 > N) || (CAUSAL && k0 + 31 > qbase);
+      tile(bufc, it, masked);
+    }
+    if (more) store_stats(BUF ^ 1);
+  };
+
+  if (it0 < n_it) {
+    stage(it0, 0);
+    load_stats(it0);
+    store_stats(0);
+  }
+  for (int it = it0; it < n_it; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_it) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   if (kcol < N) {
     uint16_t* dKrow = dK + head + (size_t)kcol * D;
     uint16_t* dVrow = dV + head + (size_t)kcol * D;
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         bf16x4 a, b;

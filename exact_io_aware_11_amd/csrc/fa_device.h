@@ -44,6 +44,21 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier for the staged pipelines.  Before the barrier this wave's
+// LDS reads and writes are complete (lgkmcnt 0) and at most VM of its vector
+// memory operations -- the newest batch of direct HBM->LDS loads -- are still
+// in flight.  (__syncthreads() would also drain those loads: its workgroup
+// fence waits for vmcnt(0), which defeats prefetching.)  The "memory" clobber
+// keeps the compiler from moving memory accesses across the barrier.
+// Waitcnt immediate (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4]
+// (7: no wait), lgkmcnt [11:8] (0: wait for all).
+template <int VM>
+__device__ __forceinline__ void barrier_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // max / sum of a value over lanes l and l ^ 32 (the two halves of a wave).
 __device__ __forceinline__ float halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
