@@ -39,11 +39,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   constexpr int BN = 128, BM = 64, TILE = BM * D;
   constexpr int LPW = TILE * 2 / 1024 / 4;  // 1 KiB direct loads per wave per tile
   constexpr int NT = D / 16, NCB = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t lq[2][TILE];   // Q tiles
-  __shared__ __attribute__((aligned(1024))) uint16_t lo[2][TILE];   // dO tiles
+  // Q and dO tiles, two buffers each.  Four separate arrays, not one indexed
+  // array: the compiler tells LDS variables apart, so reading one buffer
+  // does not wait for the direct loads still filling the other.
+  __shared__ __attribute__((aligned(1024))) uint16_t lq0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lq1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lo0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lo1[TILE];
   __shared__ __attribute__((aligned(16))) float lst[2][2][BM];      // [buffer][LSE*log2e, delta]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   uint32_t bh, kblk;
   map_block(blockIdx.x, n_kblk, total, false, bh, kblk);
@@ -93,27 +99,47 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   }
   const int n_it = (N + BM - 1) / BM;
   const int it0 = CAUSAL ? ((int)kblk * BN) / BM : 0;
-  auto stage = [&](int it, int buf) {  // rows past N read row N - 1 (masked)
+  // Rows past N read row N - 1: finite values whose probabilities the +inf
+  // LSE below turns into exact zeros.  A tile index past the end is harmless
+  // (its rows clamp the same way), so the last step stages unconditionally.
+  // Load L (0 .. 2 LPW - 1) of this wave's share: chunk L / 2 of Q (L even)
+  // or of dO (L odd).
+  auto qtile = [&](auto bufc) -> uint16_t* {
+    if constexpr (decltype(bufc)::value == 0) return lq0;
+    else return lq1;
+  };
+  auto otile = [&](auto bufc) -> uint16_t* {
+    if constexpr (decltype(bufc)::value == 0) return lo0;
+    else return lo1;
+  };
+  auto stage_one = [&](int it, auto bufc, int L) {
+    const int x = L >> 1, row = min(it * BM + grow[x], N - 1);
+    const uint16_t* src = ((L & 1) ? dOh : Qh) + (size_t)row * D + gcol[x];
+    uint16_t* dst = ((L & 1) ? otile(bufc) : qtile(bufc)) + (wave * LPW + x) * 512;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
+  auto stage = [&](int it, auto bufc) {
 #pragma unroll
-    for (int x = 0; x < LPW; ++x) {
-      const int row = min(it * BM + grow[x], N - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(Qh + (size_t)row * D + gcol[x]),
-          (__attribute__((address_space(3))) void*)(lq[buf] + (wave * LPW + x) * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(dOh + (size_t)row * D + gcol[x]),
-          (__attribute__((address_space(3))) void*)(lo[buf] + (wave * LPW + x) * 512), 16, 0, 0);
-    }
+    for (int L = 0; L < 2 * LPW; ++L) stage_one(it, bufc, L);
   };
-  float sreg = 0.f;  // threads 0..127 carry one LSE*log2e (0..63) or delta (64..127)
+  // Threads 0..127 carry one LSE (0..63) or delta (64..127) of the next tile
+  // in a register; it is used (scaled, stored to LDS) only at the end of the
+  // current tile, so the load's latency hides behind the whole tile.
+  float sreg = 0.f;
+  const float* stat_src = wave == 0 ? LSEh : Dh;  // wave-uniform: stays in scalar registers
   auto load_stats = [&](int it) {
-    if (tid < 2 * BM) {
-      const int q = it * BM + (tid & (BM - 1));
-      sreg = q < N ? (tid < BM ? LSEh[q] * kLog2e : Dh[q]) : 0.f;
-    }
+    const int q = it * BM + (tid & (BM - 1));
+    if (tid < 2 * BM && q < N) sreg = stat_src[q];
   };
-  auto store_stats = [&](int buf) {
-    if (tid < 2 * BM) lst[buf][tid / BM][tid & (BM - 1)] = sreg;
+  // Query rows past N get LSE = +inf and delta = 0, so their P and dS are
+  // exactly zero and no bounds test is needed on the query side.  Key columns
+  // past N (K, V rows zero) only reach dK/dV columns that are never written.
+  auto store_stats = [&](int it, int buf) {
+    const int q = it * BM + (tid & (BM - 1));
+    if (tid < 2 * BM)
+      lst[buf][tid / BM][tid & (BM - 1)] =
+          tid < BM ? (q < N ? sreg * kLog2e : __builtin_inff()) : (q < N ? sreg : 0.f);
   };
 
   f32x16 adk[NCB], adv[NCB];
@@ -135,12 +161,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   f32x16 s[2], dp[2];
   bf16x8 pb[2][2], db[2][2];
 
-  auto tile = [&](auto bufc, int it, bool masked) {
+  // Causal masking (key > query -> P = 0) is compiled only into the variant
+  // used for the two query tiles that can straddle this block's diagonal.
+  auto tile = [&](auto bufc, auto maskc, int it) {
     constexpr int BUF = decltype(bufc)::value;
-    const uint16_t* Qt = lq[BUF];
-    const uint16_t* Ot = lo[BUF];
+    constexpr bool masked = CAUSAL && decltype(maskc)::value;
+    const uint16_t* Qt = qtile(bufc);
+    const uint16_t* Ot = otile(bufc);
     const int qbase = it * BM;
-    constexpr int NA = 2 * NT, NB = 4 * NCB, DEPTH = 6;
+    constexpr int NA = 2 * NT, NB = 4 * NCB, DEPTH = 4;
     // operand fetches
     auto fetch_a = [&](int qb, int k) -> bf16x8 {  // k-th product of G_A(qb)
       const uint16_t* base = (k & 1) ? Ot : Qt;
@@ -177,12 +206,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     };
     // softmax-backward arithmetic of element i (0..15) of half qb
     auto soft_elem = [&](int qb, int i) {
-      const int rr = 32 * qb + 8 * (i >> 2) + 4 * g + (i & 3);
       const float l2 = l2v[i >> 2][i & 3], dl = dlv[i >> 2][i & 3];
       float p = exp2_fast(fmaf(s[qb][i], scale_log2, -l2));
-      if (masked) {
-        const int q = qbase + rr;
-        if (q >= N || kcol >= N || (CAUSAL && kcol > q)) p = 0.f;
+      if constexpr (masked) {  // row of element i: qbase + 32 qb + 4 g + 8 (i / 4) + i % 4
+        if (kcol - (qbase + 32 * qb + 4 * g) > 8 * (i >> 2) + (i & 3)) p = 0.f;
       }
       s[qb][i] = p;
       dp[qb][i] = p * (dp[qb][i] - dl);
@@ -209,17 +236,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       }
     };
     auto none = [](int) {};
+    // This wave's share of the next tile is issued one load every SEV
+    // products over the first three streams: the CU moves only about 64 B
+    // per clock from L2 into LDS, and a burst would stall the issuing waves.
+    constexpr int SEV = (2 * NA + NB) / (2 * LPW);
+    auto stage_at = [&](int op) {
+      if (op % SEV == 0) stage_one(it + 1, std::integral_constant<int, BUF ^ 1>{}, op / SEV);
+    };
     load_half_stats(0);
-    stream(false, 0, NA, none);
+    stream(false, 0, NA, [&](int k) { stage_at(k); });
     // the 16 softmax elements of a half are spread evenly over a stream
     stream(false, 1, NA, [&](int k) {
 #pragma unroll
       for (int i = k * 16 / NA; i < (k + 1) * 16 / NA; ++i) soft_elem(0, i);
+      stage_at(NA + k);
     });
     load_half_stats(1);
     stream(true, 0, NB, [&](int k) {
 #pragma unroll
       for (int i = k * 16 / NB; i < (k + 1) * 16 / NB; ++i) soft_elem(1, i);
+      stage_at(2 * NA + k);
     });
     stream(true, 1, NB, none);
   };
@@ -227,32 +263,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // Two-stage pipeline over query tiles: tile it+1 streams into the other
   // buffer while tile it is processed; one barrier per tile.  The barrier
   // waits only for this wave's loads of the tile about to be used.
-  auto step = [&](auto bufc, int it) {
+  // Every wave runs every tile of its block: in the causal prologue a wave
+  // whose keys all follow the tile's queries gets an all-zero P (a branch
+  // around it costs more registers than the one idle tile saves).
+  auto step = [&](auto bufc, auto maskc, int it) {
     constexpr int BUF = decltype(bufc)::value;
     barrier_vm<0>();  // tile `it` (loads of the previous step) visible to all
-    const bool more = it + 1 < n_it;
-    if (more) {
-      stage(it + 1, BUF ^ 1);
-      load_stats(it + 1);
-    }
-    const int qbase = it * BM;
-    const bool wave_active = !CAUSAL || qbase + BM - 1 >= k0;
-    if (wave_active) {
-      const bool masked = (qbase + BM > N) || (k0 + 32 > N) || (CAUSAL && k0 + 31 > qbase);
-      tile(bufc, it, masked);
-    }
-    if (more) store_stats(BUF ^ 1);
+    load_stats(it + 1);
+    tile(bufc, maskc, it);
+    store_stats(it + 1, BUF ^ 1);
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
-  if (it0 < n_it) {
-    stage(it0, 0);
-    load_stats(it0);
-    store_stats(0);
+  stage(it0, B0{});
+  load_stats(it0);
+  store_stats(it0, 0);
+  int it = it0;
+  if (CAUSAL) {  // tiles it0 and it0 + 1 hold every (key > query) pair of the block
+    // (it0 + 1 may lie past the end: its rows are all masked by the +inf LSE)
+    step(B0{}, std::true_type{}, it);
+    step(B1{}, std::true_type{}, it + 1);
+    it += 2;
   }
-  for (int it = it0; it < n_it; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < n_it) step(std::integral_constant<int, 1>{}, it + 1);
+  for (; it < n_it; it += 2) {
+    step(B0{}, std::false_type{}, it);
+    if (it + 1 < n_it) step(B1{}, std::false_type{}, it + 1);
   }
+  wait_vm<0>();  // the last (unused) staging lands before the workgroup's LDS is released
 
   if (kcol < N) {
     uint16_t* dKrow = dK + head + (size_t)kcol * D;

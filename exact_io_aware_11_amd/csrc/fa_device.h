@@ -53,9 +53,13 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Waitcnt immediate (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4]
 // (7: no wait), lgkmcnt [11:8] (0: wait for all).
 template <int VM>
-__device__ __forceinline__ void barrier_vm() {
+__device__ __forceinline__ void wait_vm() {
   static_assert(VM >= 0 && VM < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+template <int VM>
+__device__ __forceinline__ void barrier_vm() {
+  wait_vm<VM>();
   asm volatile("s_barrier" ::: "memory");
 }
 
