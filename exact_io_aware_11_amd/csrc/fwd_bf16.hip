@@ -39,8 +39,23 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     uint32_t n_qblk, uint32_t total, float scale, float scale_log2, float grow_thr) {
   constexpr int BM = 128, BN = 64, TILE = BN * D;  // TILE: elements of one K or V tile
   constexpr int LPW = TILE * 2 / 1024 / 4;         // 1 KiB direct loads per wave per tile
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[2][TILE];
+  // Two K and two V tile buffers as four separate arrays: the compiler tells
+  // LDS variables apart, so reading one buffer does not wait for the direct
+  // loads that are still filling another.
+  __shared__ __attribute__((aligned(1024))) uint16_t lk0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lk1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv1[TILE];
+  auto ktile = [&](auto bufc) -> uint16_t* {
+    if constexpr (decltype(bufc)::value == 0) return lk0;
+    else return lk1;
+  };
+  auto vtile = [&](auto bufc) -> uint16_t* {
+    if constexpr (decltype(bufc)::value == 0) return lv0;
+    else return lv1;
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
@@ -143,21 +158,34 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // which float32 accumulation and bf16 P hold exactly as well as values <= 1
   // -- any reference gives the same exact result.  The first tile always
   // moves m_run off -infinity.
+  // Rescale to a new reference max (rare; see rowmax_guard).
+  auto rescale = [&](float mx) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2_fast((m_run - m_new) * scale_log2);
+    l_run *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+    m_run = m_new;
+  };
+  // Online softmax (FA1 page 10.2.2; reading notes code 3-1) against a
+  // running reference max m_run.  Lazy rescale: m_run only moves when some
+  // row's tile max exceeds it by more than grow_thr (2^16 in probability);
+  // the accumulator and row sum are then rescaled by alpha = exp(m_old -
+  // m_new).  Otherwise the probabilities exp(S - m_run) may reach 2^16,
+  // which float32 accumulation and bf16 P hold exactly as well as values <= 1
+  // -- any reference gives the same exact result.  The first tile always
+  // moves m_run off -infinity.
+  auto guard = [&](float mx) {  // mx: this lane's max over its scores of the tile
+    mx = halves_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + grow_thr) != 0) rescale(mx);
+  };
   auto rowmax_guard = [&](const f32x16& s0, const f32x16& s1) {
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    mx = halves_max(mx);
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + grow_thr) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2_fast((m_run - m_new) * scale_log2);
-      l_run *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
-      m_run = m_new;
-    }
+    guard(mx);
   };
   // P = exp(S - m_run) in place; row sum over the float32 P; P in bf16 out.
   auto exps = [&](f32x16& s0, f32x16& s1, bf16x8& p00, bf16x8& p01, bf16x8& p10,
@@ -189,58 +217,111 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   };
 
   // Software pipeline: K runs one tile ahead of V.  At step j the LDS holds
-  // K_{j+1} and V_j; S_{j+1} = K_{j+1} Q^T is issued to the matrix cores
-  // interleaved with the softmax of tile j; then P_j V_j.  K_{j+2} and
-  // V_{j+1} stream in meanwhile.  One barrier per step.  Tiles
-  // [0, j_full) need no mask for any row of the workgroup and are not the
-  // last tile; the causal diagonal tiles, a ragged tail and the last tile
-  // take the general step.
+  // K_{j+1} and V_j, and the registers hold S_j = K_j Q^T whose reference max
+  // is already settled.  Tiles [0, j_full) need no mask for any row of the
+  // workgroup and are not the last tile; the causal diagonal tiles, a ragged
+  // tail and the last tile take the general step.
   const int j_full = min(min(CAUSAL ? (int)qblk * (BM / BN) : n_tiles, N / BN), n_tiles - 1);
   f32x16 sc0, sc1, sn0, sn1;
-  stage(Kh, lds_k[0], 0);
-  stage(Vh, lds_v[0], 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (n_tiles > 1) stage(Kh, lds_k[1], BN);
-  if (active(0)) scores(lds_k[0], sc0, sc1);
+  stage(Kh, lk0, 0);
+  stage(Vh, lv0, 0);
+  barrier_vm<0>();
+  if (n_tiles > 1) stage(Kh, lk1, BN);
+  if (active(0)) scores(lk0, sc0, sc1);
+  if (j_full > 0) rowmax_guard(sc0, sc1);  // tile 0 is unmasked
 
+  // Full step: one fenced stream of 32 matrix products, S_{j+1} = K_{j+1} Q^T
+  // (16, K from LDS) then O^T += V_j^T P_j^T (16, V by the transposing read,
+  // key chunk by key chunk), every operand fetched DEPTH products ahead.  The
+  // vector work rides between the products: exp, row sum and bf16 packing of
+  // P_j over products 0-23 (each key chunk of P is complete before its first
+  // PV product), the row max of S_{j+1} over products 20-31, and this wave's
+  // share of V_{j+1} and K_{j+2} is issued one load every 4 products.
+  constexpr int DEPTH = 4, NOPS = 2 * (D / 16) + 4 * (D / 32);
+  constexpr int NS = 2 * (D / 16);  // S products come first
   auto step_full = [&](auto parity, int j) {
     constexpr int P = decltype(parity)::value;  // j % 2
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces of K_{j+1} and V_j have landed
-    __syncthreads();                 // ... and everyone's
-    if (j + 1 < n_tiles) stage(Vh, lds_v[P ^ 1], (j + 1) * BN);
-    if (j + 2 < n_tiles) stage(Kh, lds_k[P], (j + 2) * BN);
-    bf16x8 p00, p01, p10, p11;
-    rowmax_guard(sc0, sc1);
-    // j + 1 < n_tiles holds (the last tile is never a full step) and every
-    // wave is active on full tiles.
-    scores(lds_k[P ^ 1], sn0, sn1);
-    exps(sc0, sc1, p00, p01, p10, p11);
-    // interleave: per S MFMA, one K read and a share of the softmax VALU
+    using PN = std::integral_constant<int, P ^ 1>;
+    barrier_vm<0>();  // this wave's pieces of K_{j+1} and V_j have landed, and everyone's
+    const uint16_t* Kt = ktile(PN{});
+    const uint16_t* Vt = vtile(parity);
+    uint16_t* Vdst = vtile(PN{});
+    uint16_t* Kdst = ktile(parity);
+    const float mneg = -m_run * scale_log2;
+    bf16x8 pk[4];
+    float mx = -INFINITY;
+    auto fetch = [&](int k) -> bf16x8 {
+      if (k < NS) return lds_read_b128(Kt + 32 * D * (k & 1) + koff[k >> 1]);
+      const int kc = (k - NS) / (D / 32), cb = (k - NS) % (D / 32);
+      return concat(lds_read_tr16(Vt + voff[cb][0] + 16 * D * kc),
+                    lds_read_tr16(Vt + voff[cb][1] + 16 * D * kc));
+    };
+    auto op = [&](int k, const bf16x8& a) {
+      if (k < NS) {
+        const int t = k >> 1;
+        if (k & 1) sn1 = mfma_bf16(a, qf[t], t == 0 ? f32x16{} : sn1);
+        else sn0 = mfma_bf16(a, qf[t], t == 0 ? f32x16{} : sn0);
+      } else {
+        const int kc = (k - NS) / (D / 32), cb = (k - NS) % (D / 32);
+        acc[cb] = mfma_bf16(a, pk[kc], acc[cb]);
+      }
+    };
+    auto exp_elem = [&](int e) {  // element e of P_j: s0[0..15] then s1[0..15]
+      f32x16& sv = (e < 16) ? sc0 : sc1;
+      const int i = e & 15;
+      sv[i] = exp2_fast(fmaf(sv[i], scale_log2, mneg));
+      l_run += sv[i];
+      if ((e & 7) == 7) pk[e >> 3] = to_bf16x8(sv, i - 7);
+    };
+    constexpr int EXP_OPS = NS + 2 * (D / 32);  // P chunk 3 is first used at product NS + 3 (D/32)
+    auto extra = [&](int k) {
+      if (k < EXP_OPS) {
 #pragma unroll
-    for (int i = 0; i < 2 * (D / 16); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        for (int e = k * 32 / EXP_OPS; e < (k + 1) * 32 / EXP_OPS; ++e) exp_elem(e);
+      }
+      if (k >= NOPS - 12) {  // row max of S_{j+1}, 32 values over the last 12 products
+        const int r = k - (NOPS - 12);
+#pragma unroll
+        for (int i = r * 16 / 12; i < (r + 1) * 16 / 12; ++i) mx = fmaxf(mx, fmaxf(sn0[i], sn1[i]));
+      }
+      if (k % 4 == 0 && k / 4 < 2 * LPW) {  // loads: V_{j+1} pieces, then K_{j+2}
+        const int x = (k / 4) % LPW;
+        const bool isv = k / 4 < LPW;
+        const int row = min((j + (isv ? 1 : 2)) * BN + grow[x], N - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)((isv ? Vh : Kh) + (size_t)row * D + gcol[x]),
+            (__attribute__((address_space(3))) void*)((isv ? Vdst : Kdst) + (wave * LPW + x) * 512), 16, 0, 0);
+      }
+    };
+    bf16x8 ring[DEPTH + 1];
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) ring[k] = fetch(k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NOPS; ++k) {
+      if (k + DEPTH < NOPS) ring[(k + DEPTH) % (DEPTH + 1)] = fetch(k + DEPTH);
+      op(k, ring[k % (DEPTH + 1)]);
+      extra(k);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    pv(lds_v[P], p00, p01, p10, p11);
     sc0 = sn0;
     sc1 = sn1;
+    if (j + 1 < j_full) guard(mx);  // a masked next tile settles its own max
   };
   auto step_masked = [&](auto parity, int j) {
     constexpr int P = decltype(parity)::value;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (j + 1 < n_tiles) stage(Vh, lds_v[P ^ 1], (j + 1) * BN);
-    if (j + 2 < n_tiles) stage(Kh, lds_k[P], (j + 2) * BN);
+    using PN = std::integral_constant<int, P ^ 1>;
+    barrier_vm<0>();
+    if (j + 1 < n_tiles) stage(Vh, vtile(PN{}), (j + 1) * BN);
+    if (j + 2 < n_tiles) stage(Kh, ktile(parity), (j + 2) * BN);
     const bool nxt = j + 1 < n_tiles && active(j + 1);
-    if (nxt) scores(lds_k[P ^ 1], sn0, sn1);
+    if (nxt) scores(ktile(PN{}), sn0, sn1);
     if (active(j)) {
       bf16x8 p00, p01, p10, p11;
       apply_mask(sc0, sc1, j * BN);
       rowmax_guard(sc0, sc1);
       exps(sc0, sc1, p00, p01, p10, p11);
-      pv(lds_v[P], p00, p01, p10, p11);
+      pv(vtile(parity), p00, p01, p10, p11);
     }
     if (nxt) {
       sc0 = sn0;
@@ -249,21 +330,22 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   };
   int j = 0;
   for (; j + 1 < j_full; j += 2) {
-    step_full(std::integral_constant<int, 0>{}, j);
-    step_full(std::integral_constant<int, 1>{}, j + 1);
+    step_full(B0{}, j);
+    step_full(B1{}, j + 1);
   }
   if (j < j_full) {
-    step_full(std::integral_constant<int, 0>{}, j);
+    step_full(B0{}, j);
     ++j;
     if (j < n_tiles) {
-      step_masked(std::integral_constant<int, 1>{}, j);
+      step_masked(B1{}, j);
       ++j;
     }
   }
   for (; j < n_tiles; j += 2) {
-    step_masked(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < n_tiles) step_masked(std::integral_constant<int, 1>{}, j + 1);
+    step_masked(B0{}, j);
+    if (j + 1 < n_tiles) step_masked(B1{}, j + 1);
   }
+  wait_vm<0>();  // no direct load may still be landing when the workgroup ends
 
   const float l_tot = halves_sum(l_run);
   const float inv = 1.f / l_tot;
