@@ -52,6 +52,20 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // keeps the compiler from moving memory accesses across the barrier.
 // Waitcnt immediate (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4]
 // (7: no wait), lgkmcnt [11:8] (0: wait for all).
+// Raw buffer resource over `bytes` bytes at `base`.  Buffer loads at byte
+// offsets past the end do not touch memory and deliver zeros (also into LDS),
+// which is how tiles running past the sequence end are padded.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes > 0 ? bytes : 0), 0x00020000);
+}
+// Direct load of 16 bytes per lane, from byte offset voff of the resource, to
+// LDS at dst + 16 * lane.  The LDS address is wave-uniform (it goes to M0).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, const void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, 0, 0, 0);
+}
+
 template <int VM>
 __device__ __forceinline__ void wait_vm() {
   static_assert(VM >= 0 && VM < 64, "vmcnt range");

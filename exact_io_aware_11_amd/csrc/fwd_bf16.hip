@@ -57,7 +57,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   uint32_t bh, qblk;
   map_block(blockIdx.x, n_qblk, total, CAUSAL, bh, qblk);
@@ -99,24 +100,24 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // [(wave*LPW + x) * 1024, +1024) of a tile buffer, lane l the 16 bytes at
   // +16 l.  Those bytes are physical chunk (16 l % 2D)/16 of tile row
   // (byte / 2D); the lane therefore fetches the logical chunk that the
-  // swizzle puts there.
-  int grow[LPW], gcol[LPW];
+  // swizzle puts there, at a byte offset in the tile that never changes.
+  uint32_t ldoff[LPW];
 #pragma unroll
   for (int x = 0; x < LPW; ++x) {
     const int byte = (wave * LPW + x) * 1024 + 16 * lane;
-    grow[x] = byte / (2 * D);
-    gcol[x] = (((byte % (2 * D)) >> 4) ^ swz<D>(grow[x])) << 3;
+    const int row = byte / (2 * D);
+    ldoff[x] = (uint32_t)(row * 2 * D + ((((byte % (2 * D)) >> 4) ^ swz<D>(row)) << 4));
   }
-  // Rows past N are fetched from row N - 1 instead (finite data; those keys
-  // are masked, so their scores never count and their P is exactly 0).
-  auto stage = [&](const uint16_t* src, uint16_t* dst, int key0) {
+  // A tile's loads go through a buffer resource that starts at the tile and
+  // ends at the head's end: rows past N arrive as zeros (those keys are
+  // masked, so their scores never count and their P is exactly 0).
+  auto tile_rsrc = [&](const uint16_t* src, int key0) __attribute__((always_inline)) {
+    return make_rsrc(src + (size_t)key0 * D, (long)(N - key0) * (2 * D));
+  };
+  auto stage = [&](const uint16_t* src, uint16_t* dst, int key0) __attribute__((always_inline)) {
+    const auto r = tile_rsrc(src, key0);
 #pragma unroll
-    for (int x = 0; x < LPW; ++x) {
-      const int row = min(key0 + grow[x], N - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src + (size_t)row * D + gcol[x]),
-          (__attribute__((address_space(3))) void*)(dst + (wave * LPW + x) * 512), 16, 0, 0);
-    }
+    for (int x = 0; x < LPW; ++x) load_lds16(r, dst + (wave * LPW + x) * 512, ldoff[x]);
   };
 
   f32x16 acc[D / 32];
@@ -124,8 +125,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  auto active = [&](int j) { return !CAUSAL || j * BN <= q0 + 31; };
-  auto scores = [&](const uint16_t* Kt, f32x16& s0, f32x16& s1) {
+  auto scores = [&](const uint16_t* Kt, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
     s0 = mfma_bf16(lds_read_b128(Kt + koff[0]), qf[0], f32x16{});
     s1 = mfma_bf16(lds_read_b128(Kt + 32 * D + koff[0]), qf[0], f32x16{});
 #pragma unroll
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // Online softmax of tile j's scores, then O^T += V_j^T P_j^T.
   // O^T += V_j^T P_j^T with P_j in bf16 (the B operand exactly as the
   // accumulator layout left it; V read transposed in the same key order).
-  auto pv = [&](const uint16_t* Vt, bf16x8 p00, bf16x8 p01, bf16x8 p10, bf16x8 p11) {
+  auto pv = [&](const uint16_t* Vt, bf16x8 p00, bf16x8 p01, bf16x8 p10, bf16x8 p11) __attribute__((always_inline)) {
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) {
       const uint16_t* vb = Vt + voff[cb][0];
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // -- any reference gives the same exact result.  The first tile always
   // moves m_run off -infinity.
   // Rescale to a new reference max (rare; see rowmax_guard).
-  auto rescale = [&](float mx) {
+  auto rescale = [&](float mx) __attribute__((always_inline)) {
     const float m_new = fmaxf(m_run, mx);
     const float alpha = exp2_fast((m_run - m_new) * scale_log2);
     l_run *= alpha;
@@ -177,11 +177,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // which float32 accumulation and bf16 P hold exactly as well as values <= 1
   // -- any reference gives the same exact result.  The first tile always
   // moves m_run off -infinity.
-  auto guard = [&](float mx) {  // mx: this lane's max over its scores of the tile
+  auto guard = [&](float mx) __attribute__((always_inline)) {  // mx: this lane's max over its scores of the tile
     mx = halves_max(mx);
     if (__builtin_amdgcn_ballot_w64(mx > m_run + grow_thr) != 0) rescale(mx);
   };
-  auto rowmax_guard = [&](const f32x16& s0, const f32x16& s1) {
+  auto rowmax_guard = [&](const f32x16& s0, const f32x16& s1) __attribute__((always_inline)) {
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   };
   // P = exp(S - m_run) in place; row sum over the float32 P; P in bf16 out.
   auto exps = [&](f32x16& s0, f32x16& s1, bf16x8& p00, bf16x8& p01, bf16x8& p10,
-                  bf16x8& p11) {
+                  bf16x8& p11) __attribute__((always_inline)) {
     const float mneg = -m_run * scale_log2;
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   };
 
   // Masked scores: keys past N, and under the causal mask keys after the query.
-  auto apply_mask = [&](f32x16& s0, f32x16& s1, int key0) {
+  auto apply_mask = [&](f32x16& s0, f32x16& s1, int key0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = key0 + 8 * (i >> 2) + 4 * g + (i & 3);
@@ -217,46 +217,66 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   };
 
   // Software pipeline: K runs one tile ahead of V.  At step j the LDS holds
-  // K_{j+1} and V_j, and the registers hold S_j = K_j Q^T whose reference max
-  // is already settled.  Tiles [0, j_full) need no mask for any row of the
-  // workgroup and are not the last tile; the causal diagonal tiles, a ragged
-  // tail and the last tile take the general step.
-  const int j_full = min(min(CAUSAL ? (int)qblk * (BM / BN) : n_tiles, N / BN), n_tiles - 1);
-  f32x16 sc0, sc1, sn0, sn1;
+  // K_{j+1} and V_j, and the registers hold S_j = K_j Q^T, masked, with its
+  // reference max settled.  Tiles [0, j_full) need no mask for any row of the
+  // workgroup; the causal diagonal tiles and a ragged tail are masked while
+  // their scores are formed.  The two score buffers swap roles with the step
+  // parity, so nothing is copied.
+  const int j_full = min(CAUSAL ? (int)qblk * (BM / BN) : n_tiles, N / BN);
+  f32x16 sa0, sa1, sb0, sb1;  // scores of even (a) and odd (b) tiles, two key halves each
+  auto sc_lo = [&](auto parity) __attribute__((always_inline)) -> f32x16& {
+    if constexpr (decltype(parity)::value == 0) return sa0;
+    else return sb0;
+  };
+  auto sc_hi = [&](auto parity) __attribute__((always_inline)) -> f32x16& {
+    if constexpr (decltype(parity)::value == 0) return sa1;
+    else return sb1;
+  };
   stage(Kh, lk0, 0);
   stage(Vh, lv0, 0);
   barrier_vm<0>();
-  if (n_tiles > 1) stage(Kh, lk1, BN);
-  if (active(0)) scores(lk0, sc0, sc1);
-  if (j_full > 0) rowmax_guard(sc0, sc1);  // tile 0 is unmasked
+  stage(Kh, lk1, BN);  // (a tile past the end arrives as zeros; never used)
+  scores(lk0, sa0, sa1);
+  if (j_full == 0) apply_mask(sa0, sa1, 0);
+  rowmax_guard(sa0, sa1);
 
-  // Full step: one fenced stream of 32 matrix products, S_{j+1} = K_{j+1} Q^T
-  // (16, K from LDS) then O^T += V_j^T P_j^T (16, V by the transposing read,
-  // key chunk by key chunk), every operand fetched DEPTH products ahead.  The
-  // vector work rides between the products: exp, row sum and bf16 packing of
-  // P_j over products 0-23 (each key chunk of P is complete before its first
-  // PV product), the row max of S_{j+1} over products 20-31, and this wave's
-  // share of V_{j+1} and K_{j+2} is issued one load every 4 products.
+  // Step j < n_tiles - 1: one fenced stream of 32 matrix products,
+  // S_{j+1} = K_{j+1} Q^T (16, K from LDS) then O^T += V_j^T P_j^T (16, V by
+  // the transposing read, key chunk by key chunk), every operand fetched
+  // DEPTH products ahead.  The vector work rides between the products: exp,
+  // row sum and bf16 packing of P_j over products 0-23 (each key chunk of P
+  // is complete before its first PV product), the mask (when tile j+1 needs
+  // one) and row max of S_{j+1} over products 20-31, and this wave's share of
+  // K_{j+2} and V_{j+1} is issued one load every 2 products early in the step,
+  // so that it has landed by the next barrier.
   constexpr int DEPTH = 4, NOPS = 2 * (D / 16) + 4 * (D / 32);
   constexpr int NS = 2 * (D / 16);  // S products come first
-  auto step_full = [&](auto parity, int j) {
+  auto step = [&](auto parity, auto maskc, int j) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;  // j % 2
+    constexpr bool MASK_NEXT = decltype(maskc)::value;
     using PN = std::integral_constant<int, P ^ 1>;
+    f32x16& sc0 = sc_lo(parity);
+    f32x16& sc1 = sc_hi(parity);
+    f32x16& sn0 = sc_lo(PN{});
+    f32x16& sn1 = sc_hi(PN{});
     barrier_vm<0>();  // this wave's pieces of K_{j+1} and V_j have landed, and everyone's
     const uint16_t* Kt = ktile(PN{});
     const uint16_t* Vt = vtile(parity);
     uint16_t* Vdst = vtile(PN{});
     uint16_t* Kdst = ktile(parity);
     const float mneg = -m_run * scale_log2;
+    const int key1 = (j + 1) * BN;
+    const auto kres = tile_rsrc(Kh, (j + 2) * BN);
+    const auto vres = tile_rsrc(Vh, (j + 1) * BN);
     bf16x8 pk[4];
     float mx = -INFINITY;
-    auto fetch = [&](int k) -> bf16x8 {
+    auto fetch = [&](int k) __attribute__((always_inline)) -> bf16x8 {
       if (k < NS) return lds_read_b128(Kt + 32 * D * (k & 1) + koff[k >> 1]);
       const int kc = (k - NS) / (D / 32), cb = (k - NS) % (D / 32);
       return concat(lds_read_tr16(Vt + voff[cb][0] + 16 * D * kc),
                     lds_read_tr16(Vt + voff[cb][1] + 16 * D * kc));
     };
-    auto op = [&](int k, const bf16x8& a) {
+    auto op = [&](int k, const bf16x8& a) __attribute__((always_inline)) {
       if (k < NS) {
         const int t = k >> 1;
         if (k & 1) sn1 = mfma_bf16(a, qf[t], t == 0 ? f32x16{} : sn1);
@@ -266,15 +286,25 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         acc[cb] = mfma_bf16(a, pk[kc], acc[cb]);
       }
     };
-    auto exp_elem = [&](int e) {  // element e of P_j: s0[0..15] then s1[0..15]
-      f32x16& sv = (e < 16) ? sc0 : sc1;
+    auto exp_elem = [&](int e) __attribute__((always_inline)) {  // element e of P_j: s0[0..15] then s1[0..15]
       const int i = e & 15;
-      sv[i] = exp2_fast(fmaf(sv[i], scale_log2, mneg));
-      l_run += sv[i];
-      if ((e & 7) == 7) pk[e >> 3] = to_bf16x8(sv, i - 7);
+      if (e < 16) {
+        sc0[i] = exp2_fast(fmaf(sc0[i], scale_log2, mneg));
+        l_run += sc0[i];
+        if ((e & 7) == 7) pk[e >> 3] = to_bf16x8(sc0, i - 7);
+      } else {
+        sc1[i] = exp2_fast(fmaf(sc1[i], scale_log2, mneg));
+        l_run += sc1[i];
+        if ((e & 7) == 7) pk[e >> 3] = to_bf16x8(sc1, i - 7);
+      }
+    };
+    auto mask_next = [&](int i) __attribute__((always_inline)) {  // element i of both halves of S_{j+1}
+      const int key = key1 + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (key >= N || (CAUSAL && key > qrow)) sn0[i] = -INFINITY;
+      if (key + 32 >= N || (CAUSAL && key + 32 > qrow)) sn1[i] = -INFINITY;
     };
     constexpr int EXP_OPS = NS + 2 * (D / 32);  // P chunk 3 is first used at product NS + 3 (D/32)
-    auto extra = [&](int k) {
+    auto extra = [&](int k) __attribute__((always_inline)) {
       if (k < EXP_OPS) {
 #pragma unroll
         for (int e = k * 32 / EXP_OPS; e < (k + 1) * 32 / EXP_OPS; ++e) exp_elem(e);
@@ -282,15 +312,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       if (k >= NOPS - 12) {  // row max of S_{j+1}, 32 values over the last 12 products
         const int r = k - (NOPS - 12);
 #pragma unroll
-        for (int i = r * 16 / 12; i < (r + 1) * 16 / 12; ++i) mx = fmaxf(mx, fmaxf(sn0[i], sn1[i]));
+        for (int i = r * 16 / 12; i < (r + 1) * 16 / 12; ++i) {
+          if constexpr (MASK_NEXT) mask_next(i);
+          mx = fmaxf(mx, fmaxf(sn0[i], sn1[i]));
+        }
+        // Pure arithmetic is placed freely by instruction selection; this
+        // empty volatile statement pins the partial max to this product.
+        asm volatile("" : "+v"(mx));
       }
-      if (k % 4 == 0 && k / 4 < 2 * LPW) {  // loads: V_{j+1} pieces, then K_{j+2}
-        const int x = (k / 4) % LPW;
-        const bool isv = k / 4 < LPW;
-        const int row = min((j + (isv ? 1 : 2)) * BN + grow[x], N - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)((isv ? Vh : Kh) + (size_t)row * D + gcol[x]),
-            (__attribute__((address_space(3))) void*)((isv ? Vdst : Kdst) + (wave * LPW + x) * 512), 16, 0, 0);
+      if (k % 2 == 0 && k / 2 < 2 * LPW) {  // loads: K_{j+2} pieces, then V_{j+1}
+        const int x = (k / 2) % LPW;
+        if (k / 2 >= LPW) load_lds16(vres, Vdst + (wave * LPW + x) * 512, ldoff[x]);
+        else load_lds16(kres, Kdst + (wave * LPW + x) * 512, ldoff[x]);
       }
     };
     bf16x8 ring[DEPTH + 1];
@@ -304,46 +337,34 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       extra(k);
       __builtin_amdgcn_sched_barrier(0);
     }
-    sc0 = sn0;
-    sc1 = sn1;
-    if (j + 1 < j_full) guard(mx);  // a masked next tile settles its own max
+    guard(mx);
   };
-  auto step_masked = [&](auto parity, int j) {
+  // Last tile: no next scores; P_j then O^T += V_j^T P_j^T.
+  auto step_last = [&](auto parity) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
-    using PN = std::integral_constant<int, P ^ 1>;
     barrier_vm<0>();
-    if (j + 1 < n_tiles) stage(Vh, vtile(PN{}), (j + 1) * BN);
-    if (j + 2 < n_tiles) stage(Kh, ktile(parity), (j + 2) * BN);
-    const bool nxt = j + 1 < n_tiles && active(j + 1);
-    if (nxt) scores(ktile(PN{}), sn0, sn1);
-    if (active(j)) {
-      bf16x8 p00, p01, p10, p11;
-      apply_mask(sc0, sc1, j * BN);
-      rowmax_guard(sc0, sc1);
-      exps(sc0, sc1, p00, p01, p10, p11);
-      pv(vtile(parity), p00, p01, p10, p11);
-    }
-    if (nxt) {
-      sc0 = sn0;
-      sc1 = sn1;
-    }
+    bf16x8 p00, p01, p10, p11;
+    exps(sc_lo(parity), sc_hi(parity), p00, p01, p10, p11);
+    pv(vtile(parity), p00, p01, p10, p11);
   };
+  // Steps whose next tile is full, then the rest (masking the next tile's
+  // scores is correct for any tile, just slower), then the last tile.
+  using NOMASK = std::false_type;
+  using MASK = std::true_type;
   int j = 0;
-  for (; j + 1 < j_full; j += 2) {
-    step_full(B0{}, j);
-    step_full(B1{}, j + 1);
+  for (; j + 2 < j_full; j += 2) {
+    step(B0{}, NOMASK{}, j);
+    step(B1{}, NOMASK{}, j + 1);
   }
-  if (j < j_full) {
-    step_full(B0{}, j);
-    ++j;
-    if (j < n_tiles) {
-      step_masked(B1{}, j);
-      ++j;
-    }
+  for (; j + 2 < n_tiles; j += 2) {
+    step(B0{}, MASK{}, j);
+    step(B1{}, MASK{}, j + 1);
   }
-  for (; j < n_tiles; j += 2) {
-    step_masked(B0{}, j);
-    if (j + 1 < n_tiles) step_masked(B1{}, j + 1);
+  if (j + 1 < n_tiles) {  // two tiles left
+    step(B0{}, MASK{}, j);
+    step_last(B1{});
+  } else {
+    step_last(B0{});
   }
   wait_vm<0>();  // no direct load may still be landing when the workgroup ends
 
