@@ -312,16 +312,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dq_bf16_kernel(
+__global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
     int N, uint32_t n_qblk, uint32_t total, float scale, float scale_log2) {
-  constexpr int BM = 128, BN = 64, CH = D / 8, TILE = BN * D;
-  constexpr int PER = BN * CH / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [buffer][K, V]
+  constexpr int BM = 128, BN = 64, TILE = BN * D;
+  constexpr int LPW = TILE * 2 / 1024 / 4;  // 1 KiB direct loads per wave per tile and tensor
+  constexpr int NT = D / 16, NCB = D / 32;
+  // K and V tiles, two buffers each, as four separate arrays (reading one
+  // buffer must not wait for the direct loads filling the other).
+  __shared__ __attribute__((aligned(1024))) uint16_t lk0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lk1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv1[TILE];
+  auto ktile = [&](auto bufc) -> uint16_t* {
+    if constexpr (decltype(bufc)::value == 0) return lk0;
+    else return lk1;
+  };
+  auto vtile = [&](auto bufc) -> uint16_t* {
+    if constexpr (decltype(bufc)::value == 0) return lv0;
+    else return lv1;
+  };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   uint32_t bh, qblk;
   map_block(blockIdx.x, n_qblk, total, CAUSAL, bh, qblk);
@@ -330,11 +345,12 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dq_bf16_kernel(
   const uint16_t* Vh = V + head;
 
   const int q0 = (int)qblk * BM + wave * 32;
-  const int qrow = q0 + r32;
+  const int qrow = q0 + r32;  // this lane's query (C-layout column)
 
-  bf16x8 qf[D / 16], of[D / 16];
+  // Q and dO rows as the B operands of S^T = K Q^T and dP^T = V dO^T.
+  bf16x8 qf[NT], of[NT];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
+  for (int t = 0; t < NT; ++t) {
     if (qrow < N) {
       qf[t] = *reinterpret_cast<const bf16x8*>(Q + head + (size_t)qrow * D + 16 * t + 8 * g);
       of[t] = *reinterpret_cast<const bf16x8*>(dO + head + (size_t)qrow * D + 16 * t + 8 * g);
@@ -343,100 +359,161 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dq_bf16_kernel(
       of[t] = bf16x8{};
     }
   }
+  // One query per lane column: LSE and delta are per-lane scalars.
   const float lse2 = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
   const float del = qrow < N ? Delta[(size_t)bh * N + qrow] : 0.f;
 
+  // K / V rows as A operands: row r32 (+32 b), chunk 2t + g.
+  int koff[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) koff[t] = tile_off<D>(r32, 2 * t + g);
+  // K^T by the transposing read (as V in the forward): source lane
+  // (r, c) = ((lane%16)/4, lane%4) reads key row 4g + r (+8) at head dim
+  // 32cb + 16((lane/16)%2) + 4c.
+  const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_n0 = 16 * ((lane >> 4) & 1);
+  int toff[NCB][2];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int d = 32 * cb + tr_n0 + 4 * tr_c;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) toff[cb][hf] = tile_off<D>(4 * g + tr_r + 8 * hf, d >> 3) + (d & 7);
+  }
+  // Direct loads of K and V tiles through buffer resources that end at the
+  // head's end (rows past N arrive as zeros: their K rows add nothing to dQ).
+  uint32_t ldoff[LPW];
+#pragma unroll
+  for (int x = 0; x < LPW; ++x) {
+    const int byte = (wave * LPW + x) * 1024 + 16 * lane;
+    const int row = byte / (2 * D);
+    ldoff[x] = (uint32_t)(row * 2 * D + ((((byte % (2 * D)) >> 4) ^ swz<D>(row)) << 4));
+  }
+  auto tile_rsrc = [&](const uint16_t* src, int key0) {
+    return make_rsrc(src + (size_t)key0 * D, (long)(N - key0) * (2 * D));
+  };
+  // Load L (0 .. 2 LPW - 1): piece L / 2 of K (L even) or of V (L odd).
+  auto stage_one = [&](const __amdgpu_buffer_rsrc_t& kr, const __amdgpu_buffer_rsrc_t& vr,
+                       auto bufc, int L) {
+    const int x = L >> 1;
+    if (L & 1) load_lds16(vr, vtile(bufc) + (wave * LPW + x) * 512, ldoff[x]);
+    else load_lds16(kr, ktile(bufc) + (wave * LPW + x) * 512, ldoff[x]);
+  };
+
   const int kv_end = CAUSAL ? min(N, (int)qblk * BM + BM) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
+  // Tiles [0, j_full) are visible to every query of the block.
+  const int j_full = CAUSAL ? (int)qblk * (BM / BN) : n_tiles;
 
-  uint4 kreg[PER], vreg[PER];
-  auto gload = [&](int j) {
+  f32x16 adq[NCB];
 #pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      const int c = tid + 256 * x, row = c / CH, ch = c % CH, key = j * BN + row;
-      if (key < N) {
-        kreg[x] = *reinterpret_cast<const uint4*>(Kh + (size_t)key * D + ch * 8);
-        vreg[x] = *reinterpret_cast<const uint4*>(Vh + (size_t)key * D + ch * 8);
-      } else {
-        kreg[x] = make_uint4(0, 0, 0, 0);
-        vreg[x] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      const int c = tid + 256 * x, row = c / CH, ch = c % CH;
-      *reinterpret_cast<uint4*>(&lds[buf][0][tile_off<D>(row, ch)]) = kreg[x];
-      *reinterpret_cast<uint4*>(&lds[buf][1][tile_off<D>(row, ch)]) = vreg[x];
-    }
-  };
+  for (int cb = 0; cb < NCB; ++cb) adq[cb] = f32x16{};
 
-  const int tr_src = lane & 15, tr_r = tr_src >> 2, tr_c = tr_src & 3;
-  const int tr_n0 = 16 * ((lane >> 4) & 1);
-
-  f32x16 adq[D / 32];
-#pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb) adq[cb] = f32x16{};
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) gload(j + 1);
+  // One 32-key half b of a 64-key tile:
+  //  G_A(b): S^T = K_b Q^T and dP^T = V_b dO^T (2 NT products, A from LDS rows)
+  //  SOFT(b): P = exp2(S log2e scale - LSE log2e), dS = P (dP - delta)
+  //  G_B(b): dQ^T += K_b^T dS_b^T (2 NCB products, A by the transposing read,
+  //          B = dS straight from the C layout)
+  // Per tile: G_A(0); [G_A(1) | SOFT(0)]; [G_B(0) | SOFT(1)]; G_B(1), the
+  // softmax arithmetic of one half woven element by element into the other
+  // half's products, every operand fetched DEPTH products ahead, and the next
+  // tile's loads spread over the first three streams.
+  f32x16 s[2], dp[2];
+  bf16x8 db[2][2];
+  auto tile = [&](auto bufc, auto maskc, int j) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr bool masked = CAUSAL && decltype(maskc)::value;
+    using BN1 = std::integral_constant<int, BUF ^ 1>;
+    const uint16_t* Kt = ktile(bufc);
+    const uint16_t* Vt = vtile(bufc);
     const int key0 = j * BN;
-    const bool active = !CAUSAL || key0 <= q0 + 31;
-    if (active) {
-      const uint16_t* Kt = lds[buf][0];
-      const uint16_t* Vt = lds[buf][1];
-      const bool need_mask = (key0 + BN > N) || (q0 + 32 > N) || (CAUSAL && key0 + BN - 1 > q0);
-      bf16x8 db[2][2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-        const int krow = 32 * b + r32;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          s = mfma_bf16(lds_read_b128(Kt + tile_off<D>(krow, 2 * t + g)), qf[t], s);
-          dp = mfma_bf16(lds_read_b128(Vt + tile_off<D>(krow, 2 * t + g)), of[t], dp);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = exp2_fast(fmaf(s[i], scale_log2, -lse2));
-          if (need_mask) {
-            const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= N || qrow >= N || (CAUSAL && key > qrow)) p = 0.f;
-          }
-          dp[i] = p * (dp[i] - del);
-        }
-        db[b][0] = to_bf16x8(dp, 0);
-        db[b][1] = to_bf16x8(dp, 8);
+    const auto kr = tile_rsrc(Kh, key0 + BN);
+    const auto vr = tile_rsrc(Vh, key0 + BN);
+    constexpr int NA = 2 * NT, NB = 2 * NCB, DEPTH = 4;
+    auto fetch_a = [&](int b, int k) -> bf16x8 {  // k-th product of G_A(b)
+      const uint16_t* base = ((k & 1) ? Vt : Kt) + 32 * D * b;
+      return lds_read_b128(base + koff[k >> 1]);
+    };
+    auto fetch_b = [&](int b, int k) -> bf16x8 {  // k-th product of G_B(b)
+      const int h = k / NCB, cb = k % NCB;
+      const uint16_t* base = Kt + (32 * b + 16 * h) * D;
+      return concat(lds_read_tr16(base + toff[cb][0]), lds_read_tr16(base + toff[cb][1]));
+    };
+    auto op_a = [&](int b, int k, const bf16x8& a) {
+      const int t = k >> 1;
+      if (k & 1) dp[b] = mfma_bf16(a, of[t], t == 0 ? f32x16{} : dp[b]);
+      else s[b] = mfma_bf16(a, qf[t], t == 0 ? f32x16{} : s[b]);
+    };
+    auto op_b = [&](int b, int k, const bf16x8& a) {
+      const int h = k / NCB, cb = k % NCB;
+      adq[cb] = mfma_bf16(a, db[b][h], adq[cb]);
+    };
+    auto soft_elem = [&](int b, int i) {  // key of element i: key0 + 32 b + 8 (i / 4) + 4 g + i % 4
+      float p = exp2_fast(fmaf(s[b][i], scale_log2, -lse2));
+      if constexpr (masked) {
+        if (key0 + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3) > qrow) p = 0.f;
       }
+      dp[b][i] = p * (dp[b][i] - del);
+      if ((i & 7) == 7) db[b][i >> 3] = to_bf16x8(dp[b], i - 7);
+    };
+    auto stream = [&](bool kind_b, int b, int nops, auto extra) {
+      bf16x8 ring[DEPTH + 1];
 #pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-        const int d = 32 * cb + tr_n0 + 4 * tr_c;
-        const int ch = d >> 3, sub = d & 7;
+      for (int k = 0; k < DEPTH; ++k) ring[k] = kind_b ? fetch_b(b, k) : fetch_a(b, k);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int r0 = 32 * b + 16 * h + 4 * g + tr_r, r1 = r0 + 8;
-            const bf16x8 ak = concat(lds_read_tr16(Kt + tile_off<D>(r0, ch) + sub),
-                                     lds_read_tr16(Kt + tile_off<D>(r1, ch) + sub));
-            adq[cb] = mfma_bf16(ak, db[b][h], adq[cb]);
-          }
+      for (int k = 0; k < nops; ++k) {
+        if (k + DEPTH < nops)
+          ring[(k + DEPTH) % (DEPTH + 1)] = kind_b ? fetch_b(b, k + DEPTH) : fetch_a(b, k + DEPTH);
+        if (kind_b) op_b(b, k, ring[k % (DEPTH + 1)]);
+        else op_a(b, k, ring[k % (DEPTH + 1)]);
+        extra(k);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    if (j + 1 < n_tiles) lstore(buf ^ 1);
-    __syncthreads();
+    };
+    constexpr int SEV = (2 * NA + NB) / (2 * LPW);  // one load every SEV products
+    auto stage_at = [&](int op) {
+      if (op % SEV == 0 && op / SEV < 2 * LPW) stage_one(kr, vr, BN1{}, op / SEV);
+    };
+    stream(false, 0, NA, [&](int k) { stage_at(k); });
+    stream(false, 1, NA, [&](int k) {
+#pragma unroll
+      for (int i = k * 16 / NA; i < (k + 1) * 16 / NA; ++i) soft_elem(0, i);
+      stage_at(NA + k);
+    });
+    stream(true, 0, NB, [&](int k) {
+#pragma unroll
+      for (int i = k * 16 / NB; i < (k + 1) * 16 / NB; ++i) soft_elem(1, i);
+      stage_at(2 * NA + k);
+    });
+    stream(true, 1, NB, [](int) {});
+  };
+
+  auto step = [&](auto bufc, auto maskc, int j) {
+    barrier_vm<0>();  // tile j (this wave's loads and everyone's) is in LDS
+    tile(bufc, maskc, j);
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  {
+    const auto kr = tile_rsrc(Kh, 0);
+    const auto vr = tile_rsrc(Vh, 0);
+#pragma unroll
+    for (int L = 0; L < 2 * LPW; ++L) stage_one(kr, vr, B0{}, L);
   }
+  int j = 0;
+  for (; j + 2 <= j_full; j += 2) {
+    step(B0{}, std::false_type{}, j);
+    step(B1{}, std::false_type{}, j + 1);
+  }
+  for (; j < n_tiles; j += 2) {  // the causal diagonal tiles (masking any tile is correct)
+    step(B0{}, std::true_type{}, j);
+    if (j + 1 < n_tiles) step(B1{}, std::true_type{}, j + 1);
+  }
+  wait_vm<0>();  // the last (unused) loads land before the workgroup's LDS is released
 
   if (qrow < N) {
     uint16_t* dQrow = dQ + head + (size_t)qrow * D;
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         bf16x4 v;
