@@ -89,21 +89,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) toff[cb][hf] = tile_off<D>(4 * g + tr_r + 8 * hf, d >> 3) + (d & 7);
   }
-  // Direct HBM -> LDS staging of Q and dO tiles (see the forward kernel).
-  int grow[LPW], gcol[LPW];
+  // Direct HBM -> LDS staging of Q and dO tiles (see the forward kernel):
+  // fixed per-lane byte offsets into a buffer resource per tile.
+  uint32_t ldoff[LPW];
 #pragma unroll
   for (int x = 0; x < LPW; ++x) {
     const int byte = (wave * LPW + x) * 1024 + 16 * lane;
-    grow[x] = byte / (2 * D);
-    gcol[x] = (((byte % (2 * D)) >> 4) ^ swz<D>(grow[x])) << 3;
+    const int row = byte / (2 * D);
+    ldoff[x] = (uint32_t)(row * 2 * D + ((((byte % (2 * D)) >> 4) ^ swz<D>(row)) << 4));
   }
   const int n_it = (N + BM - 1) / BM;
   const int it0 = CAUSAL ? ((int)kblk * BN) / BM : 0;
-  // Rows past N read row N - 1: finite values whose probabilities the +inf
-  // LSE below turns into exact zeros.  A tile index past the end is harmless
-  // (its rows clamp the same way), so the last step stages unconditionally.
-  // Load L (0 .. 2 LPW - 1) of this wave's share: chunk L / 2 of Q (L even)
-  // or of dO (L odd).
+  // The resource of a tile ends at the head's end: rows past N arrive as
+  // zeros, whose probabilities the +inf LSE below turns into exact zeros.  A
+  // tile index past the end is harmless, so the last step stages
+  // unconditionally.  Load L (0 .. 2 LPW - 1) of this wave's share: piece
+  // L / 2 of Q (L even) or of dO (L odd).
   auto qtile = [&](auto bufc) -> uint16_t* {
     if constexpr (decltype(bufc)::value == 0) return lq0;
     else return lq1;
@@ -112,16 +113,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     if constexpr (decltype(bufc)::value == 0) return lo0;
     else return lo1;
   };
-  auto stage_one = [&](int it, auto bufc, int L) {
-    const int x = L >> 1, row = min(it * BM + grow[x], N - 1);
-    const uint16_t* src = ((L & 1) ? dOh : Qh) + (size_t)row * D + gcol[x];
-    uint16_t* dst = ((L & 1) ? otile(bufc) : qtile(bufc)) + (wave * LPW + x) * 512;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  auto tile_rsrc = [&](const uint16_t* src, int row0) {
+    return make_rsrc(src + (size_t)row0 * D, (long)(N - row0) * (2 * D));
+  };
+  auto stage_one = [&](const __amdgpu_buffer_rsrc_t& qr, const __amdgpu_buffer_rsrc_t& orr,
+                       auto bufc, int L) {
+    const int x = L >> 1;
+    if (L & 1) load_lds16(orr, otile(bufc) + (wave * LPW + x) * 512, ldoff[x]);
+    else load_lds16(qr, qtile(bufc) + (wave * LPW + x) * 512, ldoff[x]);
   };
   auto stage = [&](int it, auto bufc) {
+    const auto qr = tile_rsrc(Qh, it * BM);
+    const auto orr = tile_rsrc(dOh, it * BM);
 #pragma unroll
-    for (int L = 0; L < 2 * LPW; ++L) stage_one(it, bufc, L);
+    for (int L = 0; L < 2 * LPW; ++L) stage_one(qr, orr, bufc, L);
   };
   // Threads 0..127 carry one LSE (0..63) or delta (64..127) of the next tile
   // in a register; it is used (scaled, stored to LDS) only at the end of the
@@ -240,8 +245,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     // products over the first three streams: the CU moves only about 64 B
     // per clock from L2 into LDS, and a burst would stall the issuing waves.
     constexpr int SEV = (2 * NA + NB) / (2 * LPW);
+    const auto qr = tile_rsrc(Qh, (it + 1) * BM);
+    const auto orr = tile_rsrc(dOh, (it + 1) * BM);
     auto stage_at = [&](int op) {
-      if (op % SEV == 0) stage_one(it + 1, std::integral_constant<int, BUF ^ 1>{}, op / SEV);
+      if (op % SEV == 0) stage_one(qr, orr, std::integral_constant<int, BUF ^ 1>{}, op / SEV);
     };
     load_half_stats(0);
     stream(false, 0, NA, [&](int k) { stage_at(k); });
