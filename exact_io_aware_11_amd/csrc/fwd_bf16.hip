@@ -32,13 +32,13 @@
 
 namespace fa {
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+template <int D, bool CAUSAL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int N,
     uint32_t n_qblk, uint32_t total, float scale, float scale_log2, float grow_thr) {
-  constexpr int BM = 128, BN = 64, TILE = BN * D;  // TILE: elements of one K or V tile
-  constexpr int LPW = TILE * 2 / 1024 / 4;         // 1 KiB direct loads per wave per tile
+  constexpr int BM = 32 * WAVES, BN = 64, TILE = BN * D;  // TILE: elements of one K or V tile
+  constexpr int LPW = TILE * 2 / 1024 / WAVES;            // 1 KiB direct loads per wave per tile
   // Two K and two V tile buffers as four separate arrays: the compiler tells
   // LDS variables apart, so reading one buffer does not wait for the direct
   // loads that are still filling another.
@@ -269,7 +269,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const auto kres = tile_rsrc(Kh, (j + 2) * BN);
     const auto vres = tile_rsrc(Vh, (j + 1) * BN);
     bf16x8 pk[4];
-    float mx = -INFINITY;
     auto fetch = [&](int k) __attribute__((always_inline)) -> bf16x8 {
       if (k < NS) return lds_read_b128(Kt + 32 * D * (k & 1) + koff[k >> 1]);
       const int kc = (k - NS) / (D / 32), cb = (k - NS) % (D / 32);
@@ -286,39 +285,57 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         acc[cb] = mfma_bf16(a, pk[kc], acc[cb]);
       }
     };
-    auto exp_elem = [&](int e) __attribute__((always_inline)) {  // element e of P_j: s0[0..15] then s1[0..15]
+    // Element e of P_j (s0[0..15], then s1[0..15]) in three phases placed in
+    // three consecutive products, so that no instruction waits on the one
+    // just before it: (a) the scaled, shifted score; (b) its exp; (c) the row
+    // sum (two partial sums) and, closing a key chunk, the bf16 packing.  The
+    // empty volatile statements pin each phase to its product.
+    float lsum[2] = {0.f, 0.f};
+    auto pin = [](float& x) __attribute__((always_inline)) { asm volatile("" : "+v"(x)); };
+    auto phase = [&](int e, int ph) __attribute__((always_inline)) {
+      f32x16& sv = (e < 16) ? sc0 : sc1;
       const int i = e & 15;
-      if (e < 16) {
-        sc0[i] = exp2_fast(fmaf(sc0[i], scale_log2, mneg));
-        l_run += sc0[i];
-        if ((e & 7) == 7) pk[e >> 3] = to_bf16x8(sc0, i - 7);
+      float x = sv[i];
+      if (ph == 0) {
+        pin(x);
+        x = fmaf(x, scale_log2, mneg);
+        pin(x);
+      } else if (ph == 1) {
+        x = exp2_fast(x);
+        pin(x);
       } else {
-        sc1[i] = exp2_fast(fmaf(sc1[i], scale_log2, mneg));
-        l_run += sc1[i];
-        if ((e & 7) == 7) pk[e >> 3] = to_bf16x8(sc1, i - 7);
+        lsum[e & 1] += x;
       }
+      sv[i] = x;
+      if (ph == 2 && (e & 7) == 7) pk[e >> 3] = to_bf16x8(sv, i - 7);
     };
     auto mask_next = [&](int i) __attribute__((always_inline)) {  // element i of both halves of S_{j+1}
       const int key = key1 + 8 * (i >> 2) + 4 * g + (i & 3);
       if (key >= N || (CAUSAL && key > qrow)) sn0[i] = -INFINITY;
       if (key + 32 >= N || (CAUSAL && key + 32 > qrow)) sn1[i] = -INFINITY;
     };
-    constexpr int EXP_OPS = NS + 2 * (D / 32);  // P chunk 3 is first used at product NS + 3 (D/32)
+    // Elements start phase (a) over products 0 .. EXP_OPS-1; phase (c) of the
+    // last element of key chunk kc lands two products later, before product
+    // NS + kc (D/32), the chunk's first PV product.
+    constexpr int EXP_OPS = NS + 2 * (D / 32);
+    float mxp[2] = {-INFINITY, -INFINITY};
     auto extra = [&](int k) __attribute__((always_inline)) {
-      if (k < EXP_OPS) {
 #pragma unroll
-        for (int e = k * 32 / EXP_OPS; e < (k + 1) * 32 / EXP_OPS; ++e) exp_elem(e);
+      for (int ph = 0; ph < 3; ++ph) {
+        const int ks = k - ph;
+        if (ks >= 0 && ks < EXP_OPS) {
+#pragma unroll
+          for (int e = ks * 32 / EXP_OPS; e < (ks + 1) * 32 / EXP_OPS; ++e) phase(e, ph);
+        }
       }
       if (k >= NOPS - 12) {  // row max of S_{j+1}, 32 values over the last 12 products
         const int r = k - (NOPS - 12);
 #pragma unroll
         for (int i = r * 16 / 12; i < (r + 1) * 16 / 12; ++i) {
           if constexpr (MASK_NEXT) mask_next(i);
-          mx = fmaxf(mx, fmaxf(sn0[i], sn1[i]));
+          mxp[i & 1] = fmaxf(mxp[i & 1], fmaxf(sn0[i], sn1[i]));
+          pin(mxp[i & 1]);
         }
-        // Pure arithmetic is placed freely by instruction selection; this
-        // empty volatile statement pins the partial max to this product.
-        asm volatile("" : "+v"(mx));
       }
       if (k % 2 == 0 && k / 2 < 2 * LPW) {  // loads: K_{j+2} pieces, then V_{j+1}
         const int x = (k / 2) % LPW;
@@ -337,7 +354,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       extra(k);
       __builtin_amdgcn_sched_barrier(0);
     }
-    guard(mx);
+    l_run += lsum[0] + lsum[1];
+    guard(fmaxf(mxp[0], mxp[1]));
   };
   // Last tile: no next scores; P_j then O^T += V_j^T P_j^T.
   auto step_last = [&](auto parity) __attribute__((always_inline)) {
@@ -385,20 +403,25 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int WAVES>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
-  const uint32_t n_qblk = (uint32_t)((a.N + 127) / 128);
+  constexpr int BM = 32 * WAVES;
+  const uint32_t n_qblk = (uint32_t)((a.N + BM - 1) / BM);
   const uint32_t total = (uint32_t)(a.BH * n_qblk);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WAVES>), dim3(total), dim3(64 * WAVES), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, n_qblk, total, a.scale, a.scale * kLog2e,
                      kRescaleLog2 / (a.scale * kLog2e));
   return hipGetLastError();
 }
 
+#ifndef FA_FWD_WAVES
+#define FA_FWD_WAVES 4
+#endif
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_fwd_bf16_t<64, true>(a) : launch_fwd_bf16_t<64, false>(a);
-  return a.causal ? launch_fwd_bf16_t<128, true>(a) : launch_fwd_bf16_t<128, false>(a);
+  constexpr int W = FA_FWD_WAVES;
+  if (a.d == 64) return a.causal ? launch_fwd_bf16_t<64, true, W>(a) : launch_fwd_bf16_t<64, false, W>(a);
+  return a.causal ? launch_fwd_bf16_t<128, true, W>(a) : launch_fwd_bf16_t<128, false, W>(a);
 }
 
 }  // namespace fa
