@@ -28,7 +28,11 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # The bf16 forward takes row maxima of matrix-core results, which are never
 # NaN for finite inputs; without NaN semantics fmaxf needs no quieting of its
 # operands and fuses into three-input max instructions.
-FILE_FLAGS = {"fwd_bf16.hip": ["-fno-honor-nans"]}
+# In the backward kernels the score accumulators are read by vector ALU ops
+# every tile; asking the compiler to keep matrix-core results in ordinary VGPRs
+# (not accumulation registers) saves one register move per element.
+FILE_FLAGS = {"fwd_bf16.hip": ["-fno-honor-nans"],
+              "bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
