@@ -25,13 +25,13 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-I", os.path.join(ROOT, "include")]
 
 
-# The bf16 forward takes row maxima of matrix-core results, which are never
+# The forward kernels take row maxima of matrix-core results, which are never
 # NaN for finite inputs; without NaN semantics fmaxf needs no quieting of its
 # operands and fuses into three-input max instructions.
 # In the backward kernels the score accumulators are read by vector ALU ops
 # every tile; asking the compiler to keep matrix-core results in ordinary VGPRs
 # (not accumulation registers) saves one register move per element.
-FILE_FLAGS = {"fwd_bf16.hip": ["-fno-honor-nans"],
+FILE_FLAGS = {"fwd_bf16.hip": ["-fno-honor-nans"], "fwd_fp8.hip": ["-fno-honor-nans"],
               "bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 

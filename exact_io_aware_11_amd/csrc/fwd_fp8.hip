@@ -8,10 +8,14 @@
 // factors to keep values in range.  Here:
 //  * S^T = K Q^T runs on fp8 codes; the descales q_descale * k_descale and
 //    scale * log2(e) fold into the one FMA in front of v_exp_f32.
-//  * P (in [0, 1] after the running-max shift) is multiplied by 2^8 and
-//    rounded to e4m3fn for the P V product (2^8 keeps P's range inside the
-//    format's normal range, max 448); 2^-8 * v_descale is applied once in the
-//    epilogue together with 1 / l.  The row sum l is kept from the float32 P.
+//  * P is formed already multiplied by 2^8 (the factor is folded into the
+//    exponent, exp2(x + 8)) and rounded to e4m3fn for the P V product; 2^8
+//    keeps the probabilities that matter in the format's normal range.  The
+//    row sum l is kept, in the same units, from the float32 values, so the
+//    factor cancels in O = acc / l; only the LSE removes it.
+//  * Lazy rescale as in the bf16 forward, with the headroom the format
+//    allows: the reference max moves only when a score exceeds it by enough
+//    that 2^8 P could pass 448 (the largest e4m3fn value).
 //  * V^T, the A operand of O^T = V^T P^T, needs 32 keys of one head dim per
 //    lane; there is no byte-transposing LDS read in use here, so V is staged
 //    to LDS already transposed: each thread loads a 4 keys x 4 bytes block
@@ -44,7 +48,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, uint32_t n_qblk, uint32_t total,
-    float c_score, float lse_scale, float out_scale) {
+    float c_score, float lse_scale, float out_scale, float grow_thr) {
   constexpr int BM = 128, BN = 64;
   constexpr int KCH = D / 16;                 // 16-byte chunks per K row
   constexpr int KPER = BN * KCH / 256;        // K chunks per thread
@@ -164,37 +168,40 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
             if (key >= N || (CAUSAL && key > qrow)) s[b][i] = -INFINITY;
           }
       }
-      float mx = s[0][0];
+      float ma = fmaxf(s[0][0], s[1][0]), mb = fmaxf(s[0][1], s[1][1]);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int i = 2; i < 16; i += 2) {
+        ma = fmaxf(ma, fmaxf(s[0][i], s[1][i]));
+        mb = fmaxf(mb, fmaxf(s[0][i + 1], s[1][i + 1]));
+      }
+      const float mx = halves_max(fmaxf(ma, mb));
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + grow_thr) != 0) {  // rare
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2_fast((m_run - m_new) * c_score);
+        l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2_fast((m_run - m_new) * c_score);
-      const float mneg = -m_new * c_score;
-      float rs = 0.f;
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+        m_run = m_new;
+      }
+      const float mneg = 8.f - m_run * c_score;  // 2^8 P = exp2(S c - m c + 8)
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           s[b][i] = exp2_fast(fmaf(s[b][i], c_score, mneg));
-          rs += s[b][i];
+          rs[2 * b + (i & 1)] += s[b][i];
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
       i32x8 pf;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int w = 0; w < 4; ++w)
-          pf[4 * b + w] = (int)pack4_fp8(s[b][4 * w] * 256.f, s[b][4 * w + 1] * 256.f,
-                                         s[b][4 * w + 2] * 256.f, s[b][4 * w + 3] * 256.f);
+          pf[4 * b + w] = (int)pack4_fp8(s[b][4 * w], s[b][4 * w + 1], s[b][4 * w + 2], s[b][4 * w + 3]);
 #pragma unroll
       for (int cb = 0; cb < D / 32; ++cb) {
         const int drow = 32 * cb + r32;
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
         for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[cb][4 * q4 + e] * f);
         *reinterpret_cast<bf16x4*>(Orow + 32 * cb + 8 * q4 + 4 * g) = v;
       }
-    if (g == 0) LSE[(size_t)bh * N + qrow] = m_run * lse_scale + __logf(l_tot);
+    if (g == 0) LSE[(size_t)bh * N + qrow] = m_run * lse_scale + __logf(l_tot) - 8.f * kLn2;
   }
 }
 
@@ -229,10 +236,14 @@ static hipError_t fwd_fp8_t(const FwdArgs& a) {
   const uint32_t n_qblk = (uint32_t)((a.N + 127) / 128);
   const uint32_t total = (uint32_t)(a.BH * n_qblk);
   const float sdq = a.scale * a.q_descale * a.k_descale;
+  // 2^8 P <= 448 while P <= 2^(log2(448) - 8): the reference max may lag the
+  // true max by about that much (in log2 units) before a rescale is needed;
+  // log2(440 / 256) leaves room for the rounding of v_exp_f32.
+  const float headroom_log2 = 0.7814085f;  // log2(440 / 256)
   hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, n_qblk, total, sdq * kLog2e, sdq,
-                     a.v_descale * (1.f / 256.f));
+                     a.v_descale, headroom_log2 / (sdq * kLog2e));
   return hipGetLastError();
 }
 
