@@ -16,31 +16,50 @@
 //  * Lazy rescale as in the bf16 forward, with the headroom the format
 //    allows: the reference max moves only when a score exceeds it by enough
 //    that 2^8 P could pass 448 (the largest e4m3fn value).
-//  * V^T, the A operand of O^T = V^T P^T, needs 32 keys of one head dim per
-//    lane; there is no byte-transposing LDS read in use here, so V is staged
-//    to LDS already transposed: each thread loads a 4 keys x 4 bytes block
-//    with dword loads, transposes it with v_perm_b32 and stores 4 dwords,
-//    placing keys in the order the probabilities sit in the accumulator.
-// Work split, pipeline and XCD mapping are those of the bf16 forward.
+//  * Key order: the K rows of a 32-key block are fed to the matrix core
+//    permuted so that accumulator element (block b, i) of lane half g holds
+//    key 32 g + 16 b + i.  A lane's 32 probabilities are then keys
+//    32 g .. 32 g + 31 in order -- exactly the k index the P V product wants
+//    for its B operand -- and V^T (the A operand, 32 consecutive keys of one
+//    head dim per lane) comes straight from the row-major V tile by four
+//    ds_read_b64_tr_b8.
+//  * K and V tiles are staged HBM -> LDS with buffer loads (rows past N
+//    arrive as zeros), double-buffered in four separate arrays, 16-byte XOR
+//    swizzle; one fenced stream of matrix products per 64-key step with the
+//    softmax arithmetic and the loads woven in, as in the bf16 forward.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 
 namespace {
-// 16-byte-chunk XOR swizzle for LDS tiles with RB-byte rows (RB in 64/128/256).
-template <int RB>
-__device__ __forceinline__ int off8(int row, int byte) {
-  constexpr int RP = 256 / RB;      // rows per 256 bytes
-  constexpr int CM = RB / 16 - 1;   // chunk mask
-  const int s = (row / RP) & CM;
-  return row * RB + ((((byte >> 4) ^ s)) << 4) + (byte & 15);
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte-chunk XOR swizzle of a [64 keys][D bytes] tile: conflict-free for
+// the 16-byte row reads (16 consecutive rows, one chunk) and for the
+// transposing 8-byte reads (8 consecutive rows, one chunk).
+template <int D>
+__device__ __forceinline__ int sw8(int row) {
+  return (row / (256 / D)) & (D / 16 - 1);
+}
+template <int D>
+__device__ __forceinline__ int tile_byte(int row, int chunk) {
+  return row * D + 16 * (chunk ^ sw8<D>(row));
 }
 
 __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
+}
+__device__ __forceinline__ i32x4 lds_read_i32x4(const uint8_t* p) {
+  return *reinterpret_cast<const i32x4*>(p);
+}
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2*)(const_cast<uint8_t*>(p)));
 }
 }  // namespace
 
@@ -49,15 +68,26 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, uint32_t n_qblk, uint32_t total,
     float c_score, float lse_scale, float out_scale, float grow_thr) {
-  constexpr int BM = 128, BN = 64;
-  constexpr int KCH = D / 16;                 // 16-byte chunks per K row
-  constexpr int KPER = BN * KCH / 256;        // K chunks per thread
-  constexpr int VBLK = (BN / 4) * (D / 4);    // 4x4-byte V blocks per tile
-  constexpr int VPER = VBLK / 256;
-  __shared__ __attribute__((aligned(16))) uint8_t ks[2][BN * D];  // K tile, [key][d]
-  __shared__ __attribute__((aligned(16))) uint8_t vt[2][D * BN];  // V^T tile, [d][key slot]
+  constexpr int BM = 128, BN = 64, TILE = BN * D;  // TILE in bytes
+  constexpr int LPW = TILE / 1024 / 4;             // 1 KiB direct loads per wave per tile
+  constexpr int NT = D / 64, NCB = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint8_t lk0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lk1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv1[TILE];
+  auto ktile = [&](auto bufc) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (decltype(bufc)::value == 0) return lk0;
+    else return lk1;
+  };
+  auto vtile = [&](auto bufc) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (decltype(bufc)::value == 0) return lv0;
+    else return lv1;
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   uint32_t bh, qblk;
   map_block(blockIdx.x, n_qblk, total, CAUSAL, bh, qblk);
@@ -68,9 +98,9 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   const int qrow = q0 + r32;
 
   // Q as the B operand: lane holds Q[qrow][64t + 32g .. +31].
-  i32x8 qf[D / 64];
+  i32x8 qf[NT];
 #pragma unroll
-  for (int t = 0; t < D / 64; ++t) {
+  for (int t = 0; t < NT; ++t) {
     if (qrow < N) {
       const i32x4* p = reinterpret_cast<const i32x4*>(Q + head + (size_t)qrow * D + 64 * t + 32 * g);
       const i32x4 a = p[0], b = p[1];
@@ -79,147 +109,272 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
       qf[t] = i32x8{};
     }
   }
-
   const int kv_end = CAUSAL ? min(N, (int)qblk * BM + BM) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
 
-  uint4 kreg[KPER];
-  uint32_t vreg[VPER][4];
-  auto gload = [&](int j) {
+  // K as the A operand of block b: accumulator row rho reads tile row
+  // 32((rho/4)%2) + 16b + 4(rho/8) + rho%4, so that accumulator element
+  // (b, i) of lane half g is key 32g + 16b + i.  The swizzle of those rows
+  // does not depend on b, so block 1 is block 0 plus 16 rows.
+  const int kr0 = 32 * ((r32 >> 2) & 1) + 4 * (r32 >> 3) + (r32 & 3);
+  int koff[NT][2];
 #pragma unroll
-    for (int x = 0; x < KPER; ++x) {
-      const int c = tid + 256 * x, row = c / KCH, ch = c % KCH, key = j * BN + row;
-      kreg[x] = key < N ? *reinterpret_cast<const uint4*>(Kh + (size_t)key * D + ch * 16)
-                        : make_uint4(0, 0, 0, 0);
-    }
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int y = 0; y < VPER; ++y) {
-      const int x = tid + 256 * y, k4 = x / (D / 4), d4 = x % (D / 4);
+    for (int h = 0; h < 2; ++h) koff[t][h] = tile_byte<D>(kr0, 4 * t + 2 * g + h);
+  // V^T by the transposing read: in each 16-lane group q (lane / 16), source
+  // lane s reads 8 bytes of tile row 32(q/2) + 8m + s/2 at head dim
+  // 32cb + 16(q%2) + 8(s%2); output lane j then holds head dim 32cb +
+  // 16(q%2) + j of keys 32(q/2) + 8m .. +7.  Reads m and m + 2 differ by 16
+  // rows and share the swizzle.
+  const int tq = lane >> 4, ts = lane & 15;
+  int voff[NCB][2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = j * BN + 4 * k4 + r;
-        vreg[y][r] = key < N ? *reinterpret_cast<const uint32_t*>(Vh + (size_t)key * D + 4 * d4) : 0u;
-      }
-    }
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      voff[cb][m] = tile_byte<D>(32 * (tq >> 1) + 8 * m + (ts >> 1), 2 * cb + (tq & 1)) + 8 * (ts & 1);
+  // Direct HBM -> LDS staging (see the bf16 forward): fixed per-lane byte
+  // offsets into a buffer resource per tile that ends at the head's end.
+  uint32_t ldoff[LPW];
+#pragma unroll
+  for (int x = 0; x < LPW; ++x) {
+    const int byte = (wave * LPW + x) * 1024 + 16 * lane;
+    const int row = byte / D;
+    ldoff[x] = (uint32_t)(row * D + 16 * (((byte % D) >> 4) ^ sw8<D>(row)));
+  }
+  auto tile_rsrc = [&](const uint8_t* src, int key0) __attribute__((always_inline)) {
+    return make_rsrc(src + (size_t)key0 * D, (long)(N - key0) * D);
   };
-  auto lstore = [&](int buf) {
+  auto stage = [&](const uint8_t* src, uint8_t* dst, int key0) __attribute__((always_inline)) {
+    const auto r = tile_rsrc(src, key0);
 #pragma unroll
-    for (int x = 0; x < KPER; ++x) {
-      const int c = tid + 256 * x, row = c / KCH, ch = c % KCH;
-      *reinterpret_cast<uint4*>(&ks[buf][off8<D>(row, ch * 16)]) = kreg[x];
-    }
-#pragma unroll
-    for (int y = 0; y < VPER; ++y) {
-      const int x = tid + 256 * y, k4 = x / (D / 4), d4 = x % (D / 4);
-      // 4x4 byte transpose: u[c] = (V[k+0][c], V[k+1][c], V[k+2][c], V[k+3][c])
-      const uint32_t t0 = __builtin_amdgcn_perm(vreg[y][1], vreg[y][0], 0x05010400u);
-      const uint32_t t1 = __builtin_amdgcn_perm(vreg[y][1], vreg[y][0], 0x07030602u);
-      const uint32_t t2 = __builtin_amdgcn_perm(vreg[y][3], vreg[y][2], 0x05010400u);
-      const uint32_t t3 = __builtin_amdgcn_perm(vreg[y][3], vreg[y][2], 0x07030602u);
-      uint32_t u[4];
-      u[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-      u[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-      u[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-      u[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
-      // key 4*k4 of the tile sits in accumulator block b = key/32, row
-      // 8*(i/4) + 4*gg with i%4 = 0; its slot in the B operand is 32*gg + 16*b + i.
-      const int key = 4 * k4, w = key & 31;
-      const int pos = 32 * ((w >> 2) & 1) + 16 * (key >> 5) + 4 * (w >> 3);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint32_t*>(&vt[buf][off8<BN>(4 * d4 + c, pos)]) = u[c];
-    }
+    for (int x = 0; x < LPW; ++x) load_lds16(r, dst + (wave * LPW + x) * 1024, ldoff[x]);
   };
 
-  f32x16 acc[D / 32];
+  f32x16 acc[NCB];
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) gload(j + 1);
-    const int key0 = j * BN;
-    const bool active = !CAUSAL || key0 <= q0 + 31;
-    if (active) {
-      f32x16 s[2];
+  auto fetch_k = [&](const uint8_t* Kt, int b, int t) __attribute__((always_inline)) -> i32x8 {
+    const uint8_t* base = Kt + 16 * D * b;
+    const i32x4 lo = lds_read_i32x4(base + koff[t][0]);
+    const i32x4 hi = lds_read_i32x4(base + koff[t][1]);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto fetch_v = [&](const uint8_t* Vt, int cb) __attribute__((always_inline)) -> i32x8 {
+    const i32x2 a = lds_read_tr8(Vt + voff[cb][0]);
+    const i32x2 b = lds_read_tr8(Vt + voff[cb][1]);
+    const i32x2 c = lds_read_tr8(Vt + voff[cb][0] + 16 * D);
+    const i32x2 d = lds_read_tr8(Vt + voff[cb][1] + 16 * D);
+    const i32x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    const i32x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+    return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto scores = [&](const uint8_t* Kt, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        s[b] = f32x16{};
-        const int krow = 32 * b + r32;
-#pragma unroll
-        for (int t = 0; t < D / 64; ++t) {
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(&ks[buf][off8<D>(krow, 64 * t + 32 * g)]);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(&ks[buf][off8<D>(krow, 64 * t + 32 * g + 16)]);
-          s[b] = mfma_fp8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qf[t], s[b]);
-        }
-      }
-      const bool need_mask = (key0 + BN > N) || (CAUSAL && key0 + BN - 1 > q0);
-      if (need_mask) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= N || (CAUSAL && key > qrow)) s[b][i] = -INFINITY;
-          }
-      }
-      float ma = fmaxf(s[0][0], s[1][0]), mb = fmaxf(s[0][1], s[1][1]);
-#pragma unroll
-      for (int i = 2; i < 16; i += 2) {
-        ma = fmaxf(ma, fmaxf(s[0][i], s[1][i]));
-        mb = fmaxf(mb, fmaxf(s[0][i + 1], s[1][i + 1]));
-      }
-      const float mx = halves_max(fmaxf(ma, mb));
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + grow_thr) != 0) {  // rare
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2_fast((m_run - m_new) * c_score);
-        l_run *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
-        m_run = m_new;
-      }
-      const float mneg = 8.f - m_run * c_score;  // 2^8 P = exp2(S c - m c + 8)
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[b][i] = exp2_fast(fmaf(s[b][i], c_score, mneg));
-          rs[2 * b + (i & 1)] += s[b][i];
-        }
-      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-
-      i32x8 pf;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          pf[4 * b + w] = (int)pack4_fp8(s[b][4 * w], s[b][4 * w + 1], s[b][4 * w + 2], s[b][4 * w + 3]);
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-        const int drow = 32 * cb + r32;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(&vt[buf][off8<BN>(drow, 32 * g)]);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(&vt[buf][off8<BN>(drow, 32 * g + 16)]);
-        acc[cb] = mfma_fp8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf, acc[cb]);
-      }
+    for (int t = 0; t < NT; ++t) {
+      s0 = mfma_fp8(fetch_k(Kt, 0, t), qf[t], t == 0 ? f32x16{} : s0);
+      s1 = mfma_fp8(fetch_k(Kt, 1, t), qf[t], t == 0 ? f32x16{} : s1);
     }
-    if (j + 1 < n_tiles) lstore(buf ^ 1);
-    __syncthreads();
+  };
+  auto rescale = [&](float mx) __attribute__((always_inline)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2_fast((m_run - m_new) * c_score);
+    l_run *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+    m_run = m_new;
+  };
+  auto guard = [&](float mx) __attribute__((always_inline)) {
+    mx = halves_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + grow_thr) != 0) rescale(mx);  // rare
+  };
+  // Key of accumulator element (b, i): key0 + 32 g + 16 b + i.
+  auto apply_mask = [&](f32x16& s0, f32x16& s1, int key0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = key0 + 32 * g + i;
+      if (key >= N || (CAUSAL && key > qrow)) s0[i] = -INFINITY;
+      if (key + 16 >= N || (CAUSAL && key + 16 > qrow)) s1[i] = -INFINITY;
+    }
+  };
+  auto rowmax_guard = [&](const f32x16& s0, const f32x16& s1) __attribute__((always_inline)) {
+    float ma = fmaxf(s0[0], s1[0]), mb = fmaxf(s0[1], s1[1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) {
+      ma = fmaxf(ma, fmaxf(s0[i], s1[i]));
+      mb = fmaxf(mb, fmaxf(s0[i + 1], s1[i + 1]));
+    }
+    guard(fmaxf(ma, mb));
+  };
+
+  const int j_full = min(CAUSAL ? (int)qblk * (BM / BN) : n_tiles, N / BN);
+  f32x16 sa0, sa1, sb0, sb1;
+  auto sc_lo = [&](auto parity) __attribute__((always_inline)) -> f32x16& {
+    if constexpr (decltype(parity)::value == 0) return sa0;
+    else return sb0;
+  };
+  auto sc_hi = [&](auto parity) __attribute__((always_inline)) -> f32x16& {
+    if constexpr (decltype(parity)::value == 0) return sa1;
+    else return sb1;
+  };
+  stage(Kh, lk0, 0);
+  stage(Vh, lv0, 0);
+  barrier_vm<0>();
+  stage(Kh, lk1, BN);
+  scores(lk0, sa0, sa1);
+  if (j_full == 0) apply_mask(sa0, sa1, 0);
+  rowmax_guard(sa0, sa1);
+
+  // Step j < n_tiles - 1: one fenced stream, S_{j+1} (2 NT products) then
+  // O^T += V_j^T P_j^T (NCB products), operands DEPTH products ahead.  The
+  // exp / sum / fp8 packing of P_j rides on the S products (P_j is complete
+  // before the first PV product), the mask and row max of S_{j+1} on the PV
+  // products, and this wave's loads of K_{j+2} and V_{j+1} on the first ones.
+  constexpr int DEPTH = 2, NS = 2 * NT, NOPS = NS + NCB;
+  auto step = [&](auto parity, auto maskc, int j) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    constexpr bool MASK_NEXT = decltype(maskc)::value;
+    using PN = std::integral_constant<int, P ^ 1>;
+    f32x16& sc0 = sc_lo(parity);
+    f32x16& sc1 = sc_hi(parity);
+    f32x16& sn0 = sc_lo(PN{});
+    f32x16& sn1 = sc_hi(PN{});
+    barrier_vm<0>();  // K_{j+1} and V_j have landed (this wave's loads and everyone's)
+    const uint8_t* Kt = ktile(PN{});
+    const uint8_t* Vt = vtile(parity);
+    uint8_t* Kdst = ktile(parity);
+    uint8_t* Vdst = vtile(PN{});
+    const auto kres = tile_rsrc(Kh, (j + 2) * BN);
+    const auto vres = tile_rsrc(Vh, (j + 1) * BN);
+    const float mneg = 8.f - m_run * c_score;  // 2^8 P = exp2(S c - m c + 8)
+    const int key1 = (j + 1) * BN;
+    i32x8 pf;
+    float lsum[2] = {0.f, 0.f};
+    float mxp[2] = {-INFINITY, -INFINITY};
+    auto fetch = [&](int k) __attribute__((always_inline)) -> i32x8 {
+      if (k < NS) return fetch_k(Kt, k & 1, k >> 1);
+      return fetch_v(Vt, k - NS);
+    };
+    auto op = [&](int k, const i32x8& a) __attribute__((always_inline)) {
+      if (k < NS) {
+        const int t = k >> 1;
+        if (k & 1) sn1 = mfma_fp8(a, qf[t], t == 0 ? f32x16{} : sn1);
+        else sn0 = mfma_fp8(a, qf[t], t == 0 ? f32x16{} : sn0);
+      } else {
+        acc[k - NS] = mfma_fp8(a, pf, acc[k - NS]);
+      }
+    };
+    // element e of P_j: block e / 16, index e % 16
+    auto exp_elem = [&](int e) __attribute__((always_inline)) {
+      const int i = e & 15;
+      float x;
+      if (e < 16) {
+        x = exp2_fast(fmaf(sc0[i], c_score, mneg));
+        sc0[i] = x;
+      } else {
+        x = exp2_fast(fmaf(sc1[i], c_score, mneg));
+        sc1[i] = x;
+      }
+      lsum[e & 1] += x;
+      if ((e & 3) == 3) {
+        const f32x16& sv = e < 16 ? sc0 : sc1;
+        pf[e >> 2] = (int)pack4_fp8(sv[i - 3], sv[i - 2], sv[i - 1], sv[i]);
+      }
+    };
+    auto mask_next = [&](int i) __attribute__((always_inline)) {
+      const int key = key1 + 32 * g + i;
+      if (key >= N || (CAUSAL && key > qrow)) sn0[i] = -INFINITY;
+      if (key + 16 >= N || (CAUSAL && key + 16 > qrow)) sn1[i] = -INFINITY;
+    };
+    auto extra = [&](int k) __attribute__((always_inline)) {
+      if (k < NS) {
+#pragma unroll
+        for (int e = k * 32 / NS; e < (k + 1) * 32 / NS; ++e) exp_elem(e);
+      } else {
+        const int r = k - NS;
+#pragma unroll
+        for (int i = r * 16 / NCB; i < (r + 1) * 16 / NCB; ++i) {
+          if constexpr (MASK_NEXT) mask_next(i);
+          mxp[i & 1] = fmaxf(mxp[i & 1], fmaxf(sn0[i], sn1[i]));
+        }
+        asm volatile("" : "+v"(mxp[0]), "+v"(mxp[1]));
+      }
+      if (k < 2 * LPW) {  // loads: K_{j+2} pieces, then V_{j+1}
+        const int x = k % LPW;
+        if (k >= LPW) load_lds16(vres, Vdst + (wave * LPW + x) * 1024, ldoff[x]);
+        else load_lds16(kres, Kdst + (wave * LPW + x) * 1024, ldoff[x]);
+      }
+    };
+    i32x8 ring[DEPTH + 1];
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) ring[k] = fetch(k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NOPS; ++k) {
+      if (k + DEPTH < NOPS) ring[(k + DEPTH) % (DEPTH + 1)] = fetch(k + DEPTH);
+      op(k, ring[k % (DEPTH + 1)]);
+      extra(k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += lsum[0] + lsum[1];
+    guard(fmaxf(mxp[0], mxp[1]));
+  };
+  // Last tile: P_j then O^T += V_j^T P_j^T.
+  auto step_last = [&](auto parity) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    f32x16& s0 = sc_lo(parity);
+    f32x16& s1 = sc_hi(parity);
+    barrier_vm<0>();
+    const float mneg = 8.f - m_run * c_score;
+    float rs[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = exp2_fast(fmaf(s0[i], c_score, mneg));
+      s1[i] = exp2_fast(fmaf(s1[i], c_score, mneg));
+      rs[i & 1] += s0[i] + s1[i];
+    }
+    l_run += rs[0] + rs[1];
+    i32x8 pf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      pf[w] = (int)pack4_fp8(s0[4 * w], s0[4 * w + 1], s0[4 * w + 2], s0[4 * w + 3]);
+      pf[4 + w] = (int)pack4_fp8(s1[4 * w], s1[4 * w + 1], s1[4 * w + 2], s1[4 * w + 3]);
+    }
+    const uint8_t* Vt = vtile(parity);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = mfma_fp8(fetch_v(Vt, cb), pf, acc[cb]);
+  };
+
+  using NOMASK = std::false_type;
+  using MASK = std::true_type;
+  int j = 0;
+  for (; j + 2 < j_full; j += 2) {
+    step(B0{}, NOMASK{}, j);
+    step(B1{}, NOMASK{}, j + 1);
   }
+  for (; j + 2 < n_tiles; j += 2) {
+    step(B0{}, MASK{}, j);
+    step(B1{}, MASK{}, j + 1);
+  }
+  if (j + 1 < n_tiles) {
+    step(B0{}, MASK{}, j);
+    step_last(B1{});
+  } else {
+    step_last(B0{});
+  }
+  wait_vm<0>();
 
   const float l_tot = halves_sum(l_run);
   const float f = out_scale / l_tot;
   if (qrow < N) {
     uint16_t* Orow = O + head + (size_t)qrow * D;
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         bf16x4 v;
