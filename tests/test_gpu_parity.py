@@ -79,7 +79,7 @@ def test_bf16_fwd_bwd_small(N, d, causal):
     full_check_bwd(inp, 1 / math.sqrt(d), causal, f"bf16 2x3x{N}x{d}")
 
 
-@pytest.mark.parametrize("N", [1, 100, 513])
+@pytest.mark.parametrize("N", [1, 100, 513, 1000])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_fwd_small(N, d, causal):
