@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   uint32_t bh, kblk;
-  map_block(blockIdx.x, n_kblk, total, false, bh, kblk);
+  map_block(blockIdx.x, n_kblk, total, CAUSAL ? kOrderHeavyFirst : kOrderPlain, bh, kblk);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* Qh = Q + head;
   const uint16_t* dOh = dO + head;
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   uint32_t bh, qblk;
-  map_block(blockIdx.x, n_qblk, total, CAUSAL, bh, qblk);
+  map_block(blockIdx.x, n_qblk, total, CAUSAL ? kOrderHeavyLast : kOrderPlain, bh, qblk);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;

@@ -123,19 +123,29 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
   return acc;
 }
 
-// Workgroup -> (head, row block) mapping.  Workgroups are dispatched to the 8
+// Workgroup -> (head, block) mapping.  Workgroups are dispatched to the 8
 // XCDs round-robin (id % 8), each XCD with its own L2.  When the grid divides
-// by 8, XCD x is given the contiguous range of logical blocks
-// [x * total/8, (x+1) * total/8), so the row blocks of one head run on one
-// XCD at the same time and share its L2 copy of that head's K and V.  With a
-// causal mask the heaviest row blocks (most visible keys) of a head go first.
-__device__ __forceinline__ void map_block(uint32_t w, uint32_t n_blk, uint32_t total,
-                                          bool heavy_first_reverse, uint32_t& bh, uint32_t& blk) {
+// by 8, XCD x is given a contiguous range of total/8 logical blocks, so the
+// blocks of a few heads run on one XCD and share its L2 copy of those heads'
+// tensors.  Causal work is uneven (a row block i sees i+1 key tiles; a key
+// block j is seen by the row blocks from j on): there the XCD's range is
+// walked block-major across its heads, heaviest blocks first, which keeps the
+// end of the launch to light blocks.  order: 0 plain, 1 heavy blocks are the
+// last indices (row blocks), 2 heavy blocks are the first (key blocks).
+enum : int { kOrderPlain = 0, kOrderHeavyLast = 1, kOrderHeavyFirst = 2 };
+__device__ __forceinline__ void map_block(uint32_t w, uint32_t n_blk, uint32_t total, int order,
+                                          uint32_t& bh, uint32_t& blk) {
+  if ((total & 7u) == 0u && order != kOrderPlain && ((total >> 3) % n_blk) == 0u) {
+    const uint32_t hx = (total >> 3) / n_blk, r = w >> 3;
+    bh = (w & 7u) * hx + r % hx;
+    blk = order == kOrderHeavyLast ? n_blk - 1u - r / hx : r / hx;
+    return;
+  }
   uint32_t logical = w;
   if ((total & 7u) == 0u) logical = (w & 7u) * (total >> 3) + (w >> 3);
   bh = logical / n_blk;
   blk = logical - bh * n_blk;
-  if (heavy_first_reverse) blk = n_blk - 1u - blk;
+  if (order == kOrderHeavyLast) blk = n_blk - 1u - blk;
 }
 
 // 16-byte-chunk XOR swizzle of a [rows][D] bf16 tile in LDS (D = 64 or 128).

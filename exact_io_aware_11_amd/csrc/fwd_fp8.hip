@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   uint32_t bh, qblk;
-  map_block(blockIdx.x, n_qblk, total, CAUSAL, bh, qblk);
+  map_block(blockIdx.x, n_qblk, total, CAUSAL ? kOrderHeavyLast : kOrderPlain, bh, qblk);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint8_t* Kh = K + head;
   const uint8_t* Vh = V + head;
