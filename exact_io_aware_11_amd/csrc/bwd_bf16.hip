@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
