@@ -9,8 +9,8 @@ in device memory before the timed region starts.  Each kernel is bracketed by
 HIP events on the stream it runs on, so per-kernel durations are measured live.
 
 After the timed steps the forward-only workloads (bf16 causal N=8192 d=128,
-bf16 N=2048 d=64, fp8 N=16384 d=128) are timed the same way and reported in
-the same JSON line, and the CPU oracle is timed on a bounded sample of the
+bf16 N=2048 d=64, fp8 N=16384 d=128 with per-tensor scales and with e8m0
+block scales) are timed the same way and reported in the same JSON line, and the CPU oracle is timed on a bounded sample of the
 main workload on this host's cores.
 
 Prints ONE JSON line.  Only N=1 GPU is supported (--gpus > 1 exits).
@@ -33,6 +33,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOPS (bf16, fp8) and % of MI355X MFMA peak"
 MAIN = "bf16_causal_fwdbwd_b2h16n4096d128"
 EXTRA = ["bf16_causal_fwd_b2h32n8192d128", "bf16_fwd_b4h16n2048d64", "fp8_fwd_b1h32n16384d128"]
+MX_EXTRA = ("mxfp8_fwd_b1h32n16384d128", (1, 32, 16384, 128))
 
 
 def kernel_source_hash() -> str:
@@ -171,6 +172,26 @@ def time_main(w, steps, warmup, warm_s=0.0):
     return total_ms / steps, wall, per
 
 
+def time_calls(fn, reps, warmup, warm_s=0.0):
+    """Mean and median of `reps` event-timed calls of fn after warm-up."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    if warm_s > 0:
+        warm_until(fn, warm_s)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(ms) / len(ms), ms[len(ms) // 2]
+
+
 def time_fwd_only(w, reps, warmup, warm_s=0.0):
     import torch
 
@@ -181,24 +202,33 @@ def time_fwd_only(w, reps, warmup, warm_s=0.0):
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16 if w.dtype != "fp32" else torch.float32,
                     device="cuda")
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    for _ in range(warmup):
-        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, descale=inp.descale)
-    if warm_s > 0:
-        warm_until(lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, descale=inp.descale),
-                   warm_s)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    torch.cuda.synchronize()
-    for a, b in evs:
-        a.record()
-        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, descale=inp.descale)
-        b.record()
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in evs)
-    mean = sum(ms) / len(ms)
+    res = time_calls(lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, descale=inp.descale),
+                     reps, warmup, warm_s)
     del q, k, v, o, lse
     torch.cuda.empty_cache()
-    return mean, ms[len(ms) // 2]
+    return res
+
+
+def time_fwd_mx(shape, reps, warmup, warm_s=0.0):
+    """The microscaled fp8 forward (one e8m0 scale per 32 elements along each
+    product's contraction) on the same shape as the per-tensor fp8 line."""
+    import torch
+
+    import exact_io_aware_11_amd as fa
+    import fa_inputs
+
+    B, H, N, d = shape
+    mx = fa_inputs.make_mx_inputs(shape, seed=42)
+    q, k, v, qs, ks, vs = (torch.from_numpy(a).cuda() for a in (mx.q, mx.k, mx.v, mx.qs, mx.ks,
+                                                                 mx.vs))
+    o = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    res = time_calls(lambda: fa.fa_fwd_mxfp8(q, k, v, qs, ks, vs, o, lse, scale, False),
+                     reps, warmup, warm_s)
+    del q, k, v, qs, ks, vs, o, lse
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, max_heads):
@@ -328,6 +358,14 @@ def main():
                            "frac_of_peak": round(tf / PEAK_TFLOPS[x.dtype], 4),
                            "peak": PEAK_TFLOPS[x.dtype]}
             log(f"{name}: {mean:.3f} ms {tf:.1f} TFLOP/s")
+        name, shape = MX_EXTRA
+        mean, med = time_fwd_mx(shape, reps=max(10, args.steps // 2), warmup=3,
+                                warm_s=min(args.warm_seconds, 1.0))
+        tf = fa.flops_fwd(*shape, False) / (mean * 1e-3) / 1e12
+        extra[name] = {"ms": round(mean, 4), "ms_median": round(med, 4), "TFLOP/s": round(tf, 1),
+                       "frac_of_peak": round(tf / PEAK_TFLOPS["fp8"], 4),
+                       "peak": PEAK_TFLOPS["fp8"]}
+        log(f"{name}: {mean:.3f} ms {tf:.1f} TFLOP/s")
 
     cpu = None
     if not args.no_cpu:

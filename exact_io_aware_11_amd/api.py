@@ -40,18 +40,66 @@ def _check_like(name, t, shape):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_dtypes(code, inputs, outputs):
+    """The C ABI sees only pointers: make sure every buffer has the element
+    type (and so the byte size) the kernels will assume for `code`."""
+    import torch
+
+    for name, t in inputs:
+        if dtype_code(t) != code:
+            raise TypeError(f"{name} has dtype {t.dtype}, inconsistent with the other inputs")
+    want = torch.float32 if code == FA_FP32 else torch.bfloat16
+    for name, t in outputs:
+        if t.dtype != want:
+            raise TypeError(f"{name} must be {want}, got {t.dtype}")
+
+
 def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, descale=(1.0, 1.0, 1.0), stream=None):
     """Enqueue the forward pass.  Writes o ([B,H,N,d]) and lse ([B,H,N] float32)."""
     B, H, N, d = _shape(q)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         _check_like(name, t, (B, H, N, d))
     _check_like("lse", lse, (B, H, N))
+    code = dtype_code(q)
+    _check_dtypes(code, (("k", k), ("v", v)), (("o", o),))
+    if lse.dtype != __import__("torch").float32:
+        raise TypeError("lse must be float32")
     st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     B, H, N, d, float(scale), int(bool(causal)), dtype_code(q),
                     float(descale[0]), float(descale[1]), float(descale[2]),
                     _stream_handle(stream))
     if st != FA_OK:
         raise FAError(st, "fa_fwd: " + fa_status_string(st))
+
+
+def fa_fwd_mxfp8(q, k, v, q_scale, k_scale, v_scale, o, lse, scale: float, causal: bool,
+                 stream=None):
+    """Enqueue the forward pass on fp8 e4m3fn codes with e8m0 block scales:
+    q_scale, k_scale [B,H,N,4] (bytes 0 .. d/32-1 of each row used) and
+    v_scale [B,H,ceil(N/32),d] (uint8).
+    Writes o ([B,H,N,d] bfloat16) and lse ([B,H,N] float32)."""
+    import torch
+
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_like(name, t, (B, H, N, d))
+    _check_like("lse", lse, (B, H, N))
+    _check_dtypes(FA_FP8_E4M3, (("q", q), ("k", k), ("v", v)), (("o", o),))
+    if d % 32:
+        raise ValueError("d must be a multiple of 32")
+    for name, t, shape in (("q_scale", q_scale, (B, H, N, 4)),
+                           ("k_scale", k_scale, (B, H, N, 4)),
+                           ("v_scale", v_scale, (B, H, (N + 31) // 32, d))):
+        _check_like(name, t, shape)
+        if t.dtype != torch.uint8:
+            raise TypeError(f"{name} must be uint8 (e8m0 exponents)")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    st = lib.fa_fwd_mxfp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_scale.data_ptr(),
+                          k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          B, H, N, d, float(scale), int(bool(causal)), _stream_handle(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_mxfp8: " + fa_status_string(st))
 
 
 def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
@@ -64,6 +112,11 @@ def _bwd_call(fn_name, q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, caus
                     ("dk", dk), ("dv", dv)):
         _check_like(name, t, (B, H, N, d))
     _check_like("lse", lse, (B, H, N))
+    code = dtype_code(q)
+    if code == FA_FP8_E4M3:
+        raise FAError(2, f"{fn_name}: the backward takes float32 or bfloat16 tensors")
+    _check_dtypes(code, (("k", k), ("v", v), ("o", o), ("dout", dout)),
+                  (("dq", dq), ("dk", dk), ("dv", dv)))
     nbytes = workspace.numel() * workspace.element_size()
     st = getattr(lib, fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),

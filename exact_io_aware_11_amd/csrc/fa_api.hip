@@ -79,6 +79,39 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_mxfp8(const void* q, const void* k, const void* v, const void* q_scale,
+                       const void* k_scale, const void* v_scale, void* o, float* lse, int B,
+                       int H, int N, int d, float scale, int causal, void* stream) {
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  bool empty = false;
+  fa_status st = check_sizes(B, H, N, d, &empty);
+  if (st != FA_OK) return st;
+  if (!finite_pos(scale)) return FA_ERR_INVALID_ARG;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !q_scale || !k_scale || !v_scale) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return FA_ERR_INVALID_ARG;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = (long)B * H;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.q_descale = a.k_descale = a.v_descale = 1.f;
+  a.q_scale = (const uint8_t*)q_scale;
+  a.k_scale = (const uint8_t*)k_scale;
+  a.v_scale = (const uint8_t*)v_scale;
+  a.stream = (hipStream_t)stream;
+  return fa::launch_fwd_fp8(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   bool empty = false;
   if (check_sizes(B, H, N, d, &empty) != FA_OK) return 0;

@@ -42,6 +42,14 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// fp8 e4m3 product with per-lane power-of-two (e8m0) block scales: byte
+// OPA of sa scales this lane's k block of A, byte OPB of sb that of B.
+template <int OPA, int OPB>
+__device__ __forceinline__ f32x16 mfma_fp8_scaled(i32x8 a, i32x8 b, f32x16 c, uint32_t sa,
+                                                  uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPA, (int)sa, OPB, (int)sb);
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Workgroup barrier for the staged pipelines.  Before the barrier this wave's
@@ -63,6 +71,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
 // LDS at dst + 16 * lane.  The LDS address is wave-uniform (it goes to M0).
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, const void* dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, 0, 0, 0);
+}
+
+// Direct load of 4 bytes per lane (256 bytes per wave) to LDS at dst + 4 * lane.
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, const void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4,
                                            voff, 0, 0, 0);
 }
 

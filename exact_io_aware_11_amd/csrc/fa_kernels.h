@@ -18,7 +18,12 @@ struct FwdArgs {
   int N, d;
   float scale;
   bool causal;
-  float q_descale, k_descale, v_descale;  // fp8 only
+  float q_descale, k_descale, v_descale;  // fp8 with per-tensor scales
+  // fp8 with e8m0 block scales (all three set, or all null): Q and K
+  // [BH][N][4] (bytes 0 .. d/32-1 used), V [BH][ceil(N/32)][d]
+  const uint8_t* q_scale = nullptr;
+  const uint8_t* k_scale = nullptr;
+  const uint8_t* v_scale = nullptr;
   hipStream_t stream;
 };
 

@@ -16,13 +16,24 @@
 //  * Lazy rescale as in the bf16 forward, with the headroom the format
 //    allows: the reference max moves only when a score exceeds it by enough
 //    that 2^8 P could pass 448 (the largest e4m3fn value).
+//  * Operand order (probe-verified for v_mfma_scale_f32_32x32x64_f8f6f4): of
+//    the 64 k values of a product, bytes 0-15 of lanes l and l+32 form k
+//    block 0 and bytes 16-31 form k block 1; the per-lane scale of lane l
+//    (l+32) applies to block 0 (1) of its row or column.  Lane half g
+//    therefore holds k = 16g + e and k = 32 + 16g + e (e < 16), so that the
+//    two 32-wide blocks of a product are contiguous ranges -- the blocks that
+//    microscaling formats scale.
 //  * Key order: the K rows of a 32-key block are fed to the matrix core
 //    permuted so that accumulator element (block b, i) of lane half g holds
-//    key 32 g + 16 b + i.  A lane's 32 probabilities are then keys
-//    32 g .. 32 g + 31 in order -- exactly the k index the P V product wants
-//    for its B operand -- and V^T (the A operand, 32 consecutive keys of one
-//    head dim per lane) comes straight from the row-major V tile by four
-//    ds_read_b64_tr_b8.
+//    key 32 b + 16 g + i.  A lane's 32 probabilities are then, in order, the
+//    keys the P V product wants in its B operand, and V^T (the A operand)
+//    comes straight from the row-major V tile by four ds_read_b64_tr_b8.
+//  * Microscaled variant (MX): Q and K carry one power-of-two (e8m0) scale
+//    per 32 consecutive head dims of a row, V one per 32 consecutive keys of
+//    a head dim (blocks along the contraction of each product), applied by
+//    the matrix core itself; the score needs no descale then.  The explainer's
+//    V3 section names finer-grained scale management for FP8; per-tensor
+//    scales are the coarse case.
 //  * K and V tiles are staged HBM -> LDS with buffer loads (rows past N
 //    arrive as zeros), double-buffered in four separate arrays, 16-byte XOR
 //    swizzle; one fenced stream of matrix products per 64-key step with the
@@ -63,14 +74,18 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
 }
 }  // namespace
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MX>
 __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, uint32_t n_qblk, uint32_t total,
-    float c_score, float lse_scale, float out_scale, float grow_thr) {
+    const uint8_t* __restrict__ QS, const uint8_t* __restrict__ KS,
+    const uint8_t* __restrict__ VS, uint16_t* __restrict__ O, float* __restrict__ LSE, int N,
+    uint32_t n_qblk, uint32_t total, float c_score, float lse_scale, float out_scale,
+    float grow_thr) {
   constexpr int BM = 128, BN = 64, TILE = BN * D;  // TILE in bytes
   constexpr int LPW = TILE / 1024 / 4;             // 1 KiB direct loads per wave per tile
   constexpr int NT = D / 64, NCB = D / 32;
+  // One tile's K (or V) block scales: BN * D / 32 bytes, staged as 256.
+  constexpr int SB = 256;
   __shared__ __attribute__((aligned(1024))) uint8_t lk0[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lk1[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lv0[TILE];
@@ -82,6 +97,19 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   auto vtile = [&](auto bufc) __attribute__((always_inline)) -> uint8_t* {
     if constexpr (decltype(bufc)::value == 0) return lv0;
     else return lv1;
+  };
+  // block scales of the K and V tiles (MX only), two buffers each
+  __shared__ __attribute__((aligned(16))) uint8_t lks0[MX ? SB : 4];
+  __shared__ __attribute__((aligned(16))) uint8_t lks1[MX ? SB : 4];
+  __shared__ __attribute__((aligned(16))) uint8_t lvs0[MX ? SB : 4];
+  __shared__ __attribute__((aligned(16))) uint8_t lvs1[MX ? SB : 4];
+  auto kstile = [&](auto bufc) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (decltype(bufc)::value == 0) return lks0;
+    else return lks1;
+  };
+  auto vstile = [&](auto bufc) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (decltype(bufc)::value == 0) return lvs0;
+    else return lvs1;
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -97,43 +125,56 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   const int q0 = (int)qblk * BM + wave * 32;
   const int qrow = q0 + r32;
 
-  // Q as the B operand: lane holds Q[qrow][64t + 32g .. +31].
+  // Q as the B operand: lane holds Q[qrow][64t + 16g .. +15] and
+  // Q[qrow][64t + 32 + 16g .. +15].
   i32x8 qf[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (qrow < N) {
-      const i32x4* p = reinterpret_cast<const i32x4*>(Q + head + (size_t)qrow * D + 64 * t + 32 * g);
-      const i32x4 a = p[0], b = p[1];
+      const uint8_t* p = Q + head + (size_t)qrow * D + 64 * t + 16 * g;
+      const i32x4 a = *reinterpret_cast<const i32x4*>(p);
+      const i32x4 b = *reinterpret_cast<const i32x4*>(p + 32);
       qf[t] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     } else {
       qf[t] = i32x8{};
+    }
+  }
+  // MX: this row's four (D = 128) or two block scales in one word, shifted so
+  // that byte 2t is the scale of this lane's k block of product t.
+  uint32_t qsc = 0x7f7f7f7fu;
+  if constexpr (MX) {
+    if (qrow < N) {
+      uint32_t w;
+      w = *reinterpret_cast<const uint32_t*>(QS + ((size_t)bh * N + qrow) * 4);
+      qsc = w >> (8 * g);
     }
   }
   const int kv_end = CAUSAL ? min(N, (int)qblk * BM + BM) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
 
   // K as the A operand of block b: accumulator row rho reads tile row
-  // 32((rho/4)%2) + 16b + 4(rho/8) + rho%4, so that accumulator element
-  // (b, i) of lane half g is key 32g + 16b + i.  The swizzle of those rows
-  // does not depend on b, so block 1 is block 0 plus 16 rows.
-  const int kr0 = 32 * ((r32 >> 2) & 1) + 4 * (r32 >> 3) + (r32 & 3);
+  // 32b + 16((rho/4)%2) + 4(rho/8) + rho%4, so that accumulator element
+  // (b, i) of lane half g is key 32b + 16g + i.  The swizzle of those rows
+  // does not depend on b, so block 1 is block 0 plus 32 rows.  Head dims as
+  // the k index: chunks 4t + g and 4t + 2 + g of the row.
+  const int kr0 = 16 * ((r32 >> 2) & 1) + 4 * (r32 >> 3) + (r32 & 3);
   int koff[NT][2];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) koff[t][h] = tile_byte<D>(kr0, 4 * t + 2 * g + h);
+    for (int h = 0; h < 2; ++h) koff[t][h] = tile_byte<D>(kr0, 4 * t + 2 * h + g);
   // V^T by the transposing read: in each 16-lane group q (lane / 16), source
-  // lane s reads 8 bytes of tile row 32(q/2) + 8m + s/2 at head dim
-  // 32cb + 16(q%2) + 8(s%2); output lane j then holds head dim 32cb +
-  // 16(q%2) + j of keys 32(q/2) + 8m .. +7.  Reads m and m + 2 differ by 16
-  // rows and share the swizzle.
+  // lane s reads 8 bytes of tile row 16(q/2) + 8m + s/2 (+32 for m >= 2) at
+  // head dim 32cb + 16(q%2) + 8(s%2); output lane j then holds head dim
+  // 32cb + 16(q%2) + j of those 8 keys.  Reads m and m + 2 differ by 32 rows
+  // and share the swizzle.
   const int tq = lane >> 4, ts = lane & 15;
   int voff[NCB][2];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int m = 0; m < 2; ++m)
-      voff[cb][m] = tile_byte<D>(32 * (tq >> 1) + 8 * m + (ts >> 1), 2 * cb + (tq & 1)) + 8 * (ts & 1);
+      voff[cb][m] = tile_byte<D>(16 * (tq >> 1) + 8 * m + (ts >> 1), 2 * cb + (tq & 1)) + 8 * (ts & 1);
   // Direct HBM -> LDS staging (see the bf16 forward): fixed per-lane byte
   // offsets into a buffer resource per tile that ends at the head's end.
   uint32_t ldoff[LPW];
@@ -151,6 +192,37 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
 #pragma unroll
     for (int x = 0; x < LPW; ++x) load_lds16(r, dst + (wave * LPW + x) * 1024, ldoff[x]);
   };
+  // MX block scales of a tile: K scales (one 4-byte word per key, bytes
+  // 0 .. D/32-1 used) of its 64 keys and V scales [key block][D] of its two
+  // 32-key blocks, staged by waves 0 (K, 256 bytes) and 1 (V, 2 D bytes).  A
+  // tile past the end arrives as zeros (unused).
+  const int nkb = (N + 31) / 32;
+  auto kscale_rsrc = [&](int key0) __attribute__((always_inline)) {
+    return make_rsrc(KS + ((size_t)bh * N + key0) * 4, (long)(N - key0) * 4);
+  };
+  auto vscale_rsrc = [&](int key0) __attribute__((always_inline)) {
+    return make_rsrc(VS + ((size_t)bh * nkb + key0 / 32) * D, (long)(nkb - key0 / 32) * D);
+  };
+  auto stage_kscale = [&](uint8_t* dst, int key0) __attribute__((always_inline)) {
+    if constexpr (MX) {
+      if (wave == 0) load_lds4(kscale_rsrc(key0), dst, 4 * lane);
+    }
+  };
+  auto stage_vscale = [&](uint8_t* dst, int key0) __attribute__((always_inline)) {
+    if constexpr (MX) {
+      if (wave == 1) load_lds4(vscale_rsrc(key0), dst, 4 * lane);
+    }
+  };
+  // Scale word of K row kr (tile-local), shifted so byte 2t is this lane's
+  // k block of product t; V scale byte of head dim 32cb + r32, key block g.
+  auto kscale_of = [&](const uint8_t* ks, int kr) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (!MX) return 0x7f7f7f7fu;
+    else return *reinterpret_cast<const uint32_t*>(ks + 4 * kr) >> (8 * g);
+  };
+  auto vscale_of = [&](const uint8_t* vs, int cb) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (!MX) return 0x7fu;
+    else return (uint32_t)vs[g * D + 32 * cb + r32];
+  };
 
   f32x16 acc[NCB];
 #pragma unroll
@@ -158,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   auto fetch_k = [&](const uint8_t* Kt, int b, int t) __attribute__((always_inline)) -> i32x8 {
-    const uint8_t* base = Kt + 16 * D * b;
+    const uint8_t* base = Kt + 32 * D * b;
     const i32x4 lo = lds_read_i32x4(base + koff[t][0]);
     const i32x4 hi = lds_read_i32x4(base + koff[t][1]);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -166,17 +238,23 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   auto fetch_v = [&](const uint8_t* Vt, int cb) __attribute__((always_inline)) -> i32x8 {
     const i32x2 a = lds_read_tr8(Vt + voff[cb][0]);
     const i32x2 b = lds_read_tr8(Vt + voff[cb][1]);
-    const i32x2 c = lds_read_tr8(Vt + voff[cb][0] + 16 * D);
-    const i32x2 d = lds_read_tr8(Vt + voff[cb][1] + 16 * D);
+    const i32x2 c = lds_read_tr8(Vt + voff[cb][0] + 32 * D);
+    const i32x2 d = lds_read_tr8(Vt + voff[cb][1] + 32 * D);
     const i32x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
     const i32x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
     return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  auto scores = [&](const uint8_t* Kt, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
+  // S^T product t of block b (scales: byte 2t of the K and Q words).
+  auto smfma = [&](int t, const i32x8& a, const f32x16& c, uint32_t ks) __attribute__((always_inline)) {
+    if (t == 0) return mfma_fp8_scaled<0, 0>(a, qf[0], c, ks, qsc);
+    return mfma_fp8_scaled<2, 2>(a, qf[NT - 1], c, ks, qsc);
+  };
+  auto scores = [&](const uint8_t* Kt, const uint8_t* ks, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
+    const uint32_t ks0 = kscale_of(ks, kr0), ks1 = kscale_of(ks, kr0 + 32);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      s0 = mfma_fp8(fetch_k(Kt, 0, t), qf[t], t == 0 ? f32x16{} : s0);
-      s1 = mfma_fp8(fetch_k(Kt, 1, t), qf[t], t == 0 ? f32x16{} : s1);
+      s0 = smfma(t, fetch_k(Kt, 0, t), t == 0 ? f32x16{} : s0, ks0);
+      s1 = smfma(t, fetch_k(Kt, 1, t), t == 0 ? f32x16{} : s1, ks1);
     }
   };
   auto rescale = [&](float mx) __attribute__((always_inline)) {
@@ -193,13 +271,13 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     mx = halves_max(mx);
     if (__builtin_amdgcn_ballot_w64(mx > m_run + grow_thr) != 0) rescale(mx);  // rare
   };
-  // Key of accumulator element (b, i): key0 + 32 g + 16 b + i.
+  // Key of accumulator element (b, i): key0 + 32 b + 16 g + i.
   auto apply_mask = [&](f32x16& s0, f32x16& s1, int key0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = key0 + 32 * g + i;
+      const int key = key0 + 16 * g + i;
       if (key >= N || (CAUSAL && key > qrow)) s0[i] = -INFINITY;
-      if (key + 16 >= N || (CAUSAL && key + 16 > qrow)) s1[i] = -INFINITY;
+      if (key + 32 >= N || (CAUSAL && key + 32 > qrow)) s1[i] = -INFINITY;
     }
   };
   auto rowmax_guard = [&](const f32x16& s0, const f32x16& s1) __attribute__((always_inline)) {
@@ -224,9 +302,12 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   };
   stage(Kh, lk0, 0);
   stage(Vh, lv0, 0);
+  stage_kscale(lks0, 0);
+  stage_vscale(lvs0, 0);
   barrier_vm<0>();
   stage(Kh, lk1, BN);
-  scores(lk0, sa0, sa1);
+  stage_kscale(lks1, BN);
+  scores(lk0, lks0, sa0, sa1);
   if (j_full == 0) apply_mask(sa0, sa1, 0);
   rowmax_guard(sa0, sa1);
 
@@ -251,6 +332,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     uint8_t* Vdst = vtile(PN{});
     const auto kres = tile_rsrc(Kh, (j + 2) * BN);
     const auto vres = tile_rsrc(Vh, (j + 1) * BN);
+    const uint32_t ks0 = kscale_of(kstile(PN{}), kr0), ks1 = kscale_of(kstile(PN{}), kr0 + 32);
+    uint32_t vsc[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) vsc[cb] = vscale_of(vstile(parity), cb);
     const float mneg = 8.f - m_run * c_score;  // 2^8 P = exp2(S c - m c + 8)
     const int key1 = (j + 1) * BN;
     i32x8 pf;
@@ -263,10 +348,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     auto op = [&](int k, const i32x8& a) __attribute__((always_inline)) {
       if (k < NS) {
         const int t = k >> 1;
-        if (k & 1) sn1 = mfma_fp8(a, qf[t], t == 0 ? f32x16{} : sn1);
-        else sn0 = mfma_fp8(a, qf[t], t == 0 ? f32x16{} : sn0);
+        if (k & 1) sn1 = smfma(t, a, t == 0 ? f32x16{} : sn1, ks1);
+        else sn0 = smfma(t, a, t == 0 ? f32x16{} : sn0, ks0);
       } else {
-        acc[k - NS] = mfma_fp8(a, pf, acc[k - NS]);
+        acc[k - NS] = mfma_fp8_scaled<0, 0>(a, pf, acc[k - NS], vsc[k - NS], 0x7fu);
       }
     };
     // element e of P_j: block e / 16, index e % 16
@@ -287,9 +372,9 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
       }
     };
     auto mask_next = [&](int i) __attribute__((always_inline)) {
-      const int key = key1 + 32 * g + i;
+      const int key = key1 + 16 * g + i;
       if (key >= N || (CAUSAL && key > qrow)) sn0[i] = -INFINITY;
-      if (key + 16 >= N || (CAUSAL && key + 16 > qrow)) sn1[i] = -INFINITY;
+      if (key + 32 >= N || (CAUSAL && key + 32 > qrow)) sn1[i] = -INFINITY;
     };
     auto extra = [&](int k) __attribute__((always_inline)) {
       if (k < NS) {
@@ -308,6 +393,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
         const int x = k % LPW;
         if (k >= LPW) load_lds16(vres, Vdst + (wave * LPW + x) * 1024, ldoff[x]);
         else load_lds16(kres, Kdst + (wave * LPW + x) * 1024, ldoff[x]);
+      }
+      if (k == 0) {
+        stage_kscale(kstile(parity), (j + 2) * BN);
+        stage_vscale(vstile(PN{}), (j + 1) * BN);
       }
     };
     i32x8 ring[DEPTH + 1];
@@ -347,7 +436,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     }
     const uint8_t* Vt = vtile(parity);
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[cb] = mfma_fp8(fetch_v(Vt, cb), pf, acc[cb]);
+    for (int cb = 0; cb < NCB; ++cb)
+      acc[cb] = mfma_fp8_scaled<0, 0>(fetch_v(Vt, cb), pf, acc[cb], vscale_of(vstile(parity), cb), 0x7fu);
   };
 
   using NOMASK = std::false_type;
@@ -386,25 +476,32 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MX>
 static hipError_t fwd_fp8_t(const FwdArgs& a) {
   const uint32_t n_qblk = (uint32_t)((a.N + 127) / 128);
   const uint32_t total = (uint32_t)(a.BH * n_qblk);
-  const float sdq = a.scale * a.q_descale * a.k_descale;
+  // MX: the scales are inside the products; per tensor: folded in here.
+  const float sdq = MX ? a.scale : a.scale * a.q_descale * a.k_descale;
+  const float vd = MX ? 1.f : a.v_descale;
   // 2^8 P <= 448 while P <= 2^(log2(448) - 8): the reference max may lag the
   // true max by about that much (in log2 units) before a rescale is needed;
   // log2(440 / 256) leaves room for the rounding of v_exp_f32.
   const float headroom_log2 = 0.7814085f;  // log2(440 / 256)
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
-                     (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.N, n_qblk, total, sdq * kLog2e, sdq,
-                     a.v_descale, headroom_log2 / (sdq * kLog2e));
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, MX>), dim3(total), dim3(256), 0, a.stream,
+                     (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_scale,
+                     a.k_scale, a.v_scale, (uint16_t*)a.o, a.lse, a.N, n_qblk, total,
+                     sdq * kLog2e, sdq, vd, headroom_log2 / (sdq * kLog2e));
   return hipGetLastError();
 }
 
+template <bool MX>
+static hipError_t fwd_fp8_any(const FwdArgs& a) {
+  if (a.d == 64) return a.causal ? fwd_fp8_t<64, true, MX>(a) : fwd_fp8_t<64, false, MX>(a);
+  return a.causal ? fwd_fp8_t<128, true, MX>(a) : fwd_fp8_t<128, false, MX>(a);
+}
+
 hipError_t launch_fwd_fp8(const FwdArgs& a) {
-  if (a.d == 64) return a.causal ? fwd_fp8_t<64, true>(a) : fwd_fp8_t<64, false>(a);
-  return a.causal ? fwd_fp8_t<128, true>(a) : fwd_fp8_t<128, false>(a);
+  return a.q_scale ? fwd_fp8_any<true>(a) : fwd_fp8_any<false>(a);
 }
 
 }  // namespace fa

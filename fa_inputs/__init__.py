@@ -96,6 +96,82 @@ def quantize_e4m3fn(x: np.ndarray):
     return codes, float(s)
 
 
+def quantize_mx_e4m3fn(x: np.ndarray, axis: int):
+    """float32 -> (e4m3fn codes, e8m0 block scales) with blocks of 32
+    consecutive elements along `axis` (OCP microscaling convention).
+
+    Per block: amax = max |x|; shared scale 2^(floor(log2 amax) - 8) (8 is the
+    largest e4m3 exponent), stored as the byte floor(log2 amax) - 8 + 127
+    clipped to [0, 254] (0 for an all-zero block); codes = RNE(x / scale)
+    saturated to +-448.  `axis` must have a length that is a multiple of 32 or
+    is padded with zeros to one (the padding is dropped from the codes).
+    Returns codes shaped like x and scales with that axis divided by 32
+    (rounded up) -- the layout fa_fwd_mxfp8 takes.
+    """
+    import torch
+
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    ax = axis % x.ndim
+    n = x.shape[ax]
+    nb = (n + 31) // 32
+    pad = [(0, 0)] * x.ndim
+    pad[ax] = (0, nb * 32 - n)
+    xp = torch.from_numpy(np.pad(x, pad) if nb * 32 != n else x).movedim(ax, -1)
+    xb = xp.reshape(*xp.shape[:-1], nb, 32)
+    amax = xb.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, 1.0))) - 8.0,
+                    -127.0)
+    code = torch.clamp(e + 127.0, 0, 254).to(torch.uint8)
+    scale = torch.ldexp(torch.ones((), dtype=torch.float32), code.to(torch.int32) - 127)
+    y = (xb / scale[..., None]).clamp_(-E4M3_MAX, E4M3_MAX)
+    q = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(*xb.shape[:-2], nb * 32)
+    q = q[..., :n].movedim(-1, ax)
+    return np.ascontiguousarray(q.numpy()), np.ascontiguousarray(code.movedim(-1, ax).numpy())
+
+
+@dataclass
+class MXInputs:
+    """fp8 inputs with e8m0 block scales: q, k, v codes [B,H,N,d]; qs, ks
+    [B,H,N,4] (blocks along d in bytes 0 .. d/32-1, the rest 127); vs
+    [B,H,ceil(N/32),d] (blocks along N) -- the layout fa_fwd_mxfp8 takes."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    qs: np.ndarray
+    ks: np.ndarray
+    vs: np.ndarray
+
+
+def draw_spread_f32(shape, seed: int = 42, spread_log2: float = 0.0):
+    """Q, K, V ~ N(0,1) float32 from `seed` (as draw_f32); with spread > 0,
+    each row of Q and K and each head-dim channel of V (per batch and head)
+    is multiplied by 2^u, u uniform in [-spread, 0] (a second stream of the
+    same generator).  Magnitudes only shrink, so the logits stay within the
+    unspread range and the softmax stays as well conditioned as there."""
+    q, k, v = draw_f32(shape, seed, count=3)
+    if spread_log2 > 0:
+        rng = np.random.default_rng(seed + 1)
+        row = shape[:-1] + (1,)
+        chan = shape[:-2] + (1, shape[-1])
+        q, k, v = (x * np.exp2(rng.uniform(-spread_log2, 0.0, size=sz)).astype(np.float32)
+                   for x, sz in ((q, row), (k, row), (v, chan)))
+    return q, k, v
+
+
+def make_mx_inputs(shape, seed: int = 42, spread_log2: float = 0.0) -> MXInputs:
+    """draw_spread_f32's Q, K, V, block-quantized: Q and K in blocks along the
+    head dim, V in blocks along the sequence."""
+    q, k, v = draw_spread_f32(shape, seed, spread_log2)
+    (qc, qs), (kc, ks) = quantize_mx_e4m3fn(q, -1), quantize_mx_e4m3fn(k, -1)
+    vc, vs = quantize_mx_e4m3fn(v, -2)
+
+    def word(s):  # one 4-byte word per row
+        w = np.full(s.shape[:-1] + (4,), 127, np.uint8)
+        w[..., :s.shape[-1]] = s
+        return w
+    return MXInputs(qc, kc, vc, word(qs), word(ks), vs)
+
+
 @dataclass
 class Inputs:
     """Storage-format inputs for one workload.

@@ -74,6 +74,25 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int N, int d, float scale, int causal, int dtype, float q_descale,
                  float k_descale, float v_descale, void* stream);
 
+/* Forward pass on fp8 e4m3fn inputs with microscaling block scales (the
+ * finer-grained scale management the explainer's V3 section names for FP8;
+ * per-tensor scales, fa_fwd with FA_FP8_E4M3, are the coarse case).  Each
+ * block of 32 consecutive elements along a product's contraction shares one
+ * power-of-two scale stored as an e8m0 byte E (value 2^(E - 127); E = 255 is
+ * not accepted by the hardware and must not occur):
+ *   q_scale, k_scale : [B,H,N,4] bytes -- byte c (c < d/32) of row n scales
+ *                      head dims 32c .. 32c+31 (the contraction of Q K^T);
+ *                      one 4-byte word per row whatever d, the rest unused
+ *   v_scale          : [B,H,ceil(N/32),d] bytes -- block b of head dim j
+ *                      covers keys 32b .. 32b+31 (the contraction of P V)
+ * The real value of a code is decode(code) * 2^(E - 127) of its block.  The
+ * other arguments are those of fa_fwd (o is bfloat16, lse float32); q, k, v,
+ * o need 16-byte alignment, the scale arrays 4-byte alignment.  Same status
+ * codes; nothing is launched on an error. */
+fa_status fa_fwd_mxfp8(const void* q, const void* k, const void* v, const void* q_scale,
+                       const void* k_scale, const void* v_scale, void* o, float* lse, int B,
+                       int H, int N, int d, float scale, int causal, void* stream);
+
 /* Bytes of device workspace fa_bwd needs for these sizes (delta, one float32
  * per row, at the start of the workspace).  Returns 0 for invalid sizes. */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);

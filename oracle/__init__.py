@@ -24,6 +24,9 @@ eliminating IO", deep-learning-notes ch10.2; "Flash Attention V1/V2/V3" explaine
   m and l, with delta_i = dO_i . O_i.
 * :func:`decode_bf16`, :func:`decode_e4m3fn` -- exact decoders of the storage
   formats (bfloat16; OCP float8 e4m3fn times its per-tensor scale).
+* :func:`decode_mx_e4m3fn` -- e4m3fn codes times their block's power-of-two
+  (e8m0) scale: the finer-grained FP8 scaling the explainer's V3 section
+  names, in the microscaling layout (32 consecutive elements per block).
 
 Every function is pinned by tests that do not use this module's own
 arithmetic: brute force on tiny inputs, closed forms, invariants, finite
@@ -210,3 +213,21 @@ def decode_e4m3fn(codes, scale: float = 1.0) -> np.ndarray:
     lib.oracle_decode_e4m3fn(c.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)), float(scale),
                              _ptr(out), c.size)
     return out
+
+
+def decode_mx_e4m3fn(codes, scales, axis: int) -> np.ndarray:
+    """e4m3fn codes with e8m0 block scales -> exact float64 values.
+
+    Element i along `axis` belongs to block i // 32 and is decode(code) *
+    2^(E - 127), E the block's scale byte (scales has that axis of length
+    ceil(n / 32)).  Multiplying by a power of two is exact in float64.
+    """
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    e = np.ascontiguousarray(scales, dtype=np.uint8)
+    ax = axis % c.ndim
+    n = c.shape[ax]
+    if e.shape[ax] != (n + 31) // 32:
+        raise ValueError("scales must have ceil(n/32) blocks along axis")
+    expanded = np.repeat(e.astype(np.int64) - 127, 32, axis=ax)
+    expanded = np.take(expanded, np.arange(n), axis=ax)
+    return np.ldexp(decode_e4m3fn(c), expanded)

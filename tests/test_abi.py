@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
-                                    "fa_bwd_workspace_size", "fa_fwd", "fa_status_string"]
+                                    "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_mxfp8",
+                                    "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -42,6 +43,28 @@ def fwd(**kw):
     a.update(kw)
     return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
                       a["scale"], a["causal"], a["dtype"], a["qd"], a["kd"], a["vd"], a["stream"])
+
+
+def fwd_mx(**kw):
+    a = dict(q=P, k=P, v=P, qs=P, ks=P, vs=P, o=P, lse=P, B=1, H=1, N=16, d=64, scale=0.125,
+             causal=0, stream=None)
+    a.update(kw)
+    return lib.fa_fwd_mxfp8(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"],
+                            a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNSUPPORTED), (dict(d=0), INVALID), (dict(causal=3), INVALID),
+    (dict(N=-1), INVALID), (dict(scale=0.0), INVALID), (dict(scale=math.nan), INVALID),
+    (dict(qs=0), INVALID), (dict(ks=0), INVALID), (dict(vs=0), INVALID), (dict(q=0), INVALID),
+    (dict(qs=P + 1), INVALID), (dict(vs=P + 2), INVALID), (dict(v=P + 4), INVALID),
+])
+def test_fwd_mxfp8_rejects_before_launch(kw, status):
+    assert fwd_mx(**kw) == status
+
+
+def test_fwd_mxfp8_empty_is_a_noop():
+    assert fwd_mx(N=0, qs=0, ks=0, vs=0) == OK and fwd_mx(B=0) == OK
 
 
 def bwd(fn="fa_bwd", **kw):

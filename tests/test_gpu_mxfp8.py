@@ -1,0 +1,103 @@
+"""GPU parity of the microscaled fp8 forward (fa_fwd_mxfp8): e4m3fn codes
+with one e8m0 scale per 32 consecutive elements along each product's
+contraction (Q, K along d; V along the sequence), against the float64
+oracle on the exact decoded values.  Bars as for per-tensor fp8: O within
+6e-2 * max|oracle|, LSE within 1e-2 + 1e-4 |LSE|."""
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs
+import oracle
+from _util import check, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import exact_io_aware_11_amd as fa  # noqa: E402
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_mx(mx, scale, causal):
+    B, H, N, d = mx.q.shape
+    o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    fa.fa_fwd_mxfp8(dev(mx.q), dev(mx.k), dev(mx.v), dev(mx.qs), dev(mx.ks), dev(mx.vs), o, lse,
+                    scale, causal)
+    torch.cuda.synchronize()
+    return to_f64(o), to_f64(lse)
+
+
+def blocks(s, d):  # the d/32 used bytes of a per-row scale word
+    return s[..., : d // 32]
+
+
+def values(mx):
+    d = mx.q.shape[-1]
+    return (oracle.decode_mx_e4m3fn(mx.q, blocks(mx.qs, d), -1),
+            oracle.decode_mx_e4m3fn(mx.k, blocks(mx.ks, d), -1),
+            oracle.decode_mx_e4m3fn(mx.v, mx.vs, -2))
+
+
+@pytest.mark.parametrize("N", [1, 100, 513, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mxfp8_fwd_small(N, d, causal):
+    mx = fa_inputs.make_mx_inputs((1, 3, N, d), seed=13 * N + d, spread_log2=4.0)
+    tag = f"mxfp8 1x3x{N}x{d} causal={causal}"
+    say(tag)
+    o, lse = run_mx(mx, 1 / math.sqrt(d), causal)
+    qs, ks, vs = values(mx)
+    o_ref, lse_ref = oracle.attn_fwd(qs, ks, vs, 1 / math.sqrt(d), causal)
+    check(f"{tag} O", o, o_ref, "fp8")
+    check(f"{tag} LSE", lse, lse_ref, "fp8", lse=True)
+
+
+def test_full_mxfp8_fwd_b1h32n16384d128():
+    w = fa_inputs.WORKLOADS["fp8_fwd_b1h32n16384d128"]
+    mx = fa_inputs.make_mx_inputs(w.shape, seed=42)
+    o, lse = run_mx(mx, w.scale, w.causal)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = np.unique(np.concatenate([np.random.default_rng(0).choice(w.N, 16, replace=False),
+                                     [0, 1, 31, 32, 63, 64, w.N // 2, w.N - 1]]))
+    for h in (0, 31):
+        qs = oracle.decode_mx_e4m3fn(mx.q[0, h], blocks(mx.qs[0, h], w.d), -1)
+        ks = oracle.decode_mx_e4m3fn(mx.k[0, h], blocks(mx.ks[0, h], w.d), -1)
+        vs = oracle.decode_mx_e4m3fn(mx.v[0, h], mx.vs[0, h], -2)
+        o_ref, lse_ref = oracle.attn_fwd_rows(qs, ks, vs, rows, w.scale, w.causal)
+        check(f"mxfp8 full head {h} O rows", o[0, h, rows], o_ref, "fp8")
+        check(f"mxfp8 full head {h} LSE rows", lse[0, h, rows], lse_ref, "fp8", lse=True)
+
+
+def test_mxfp8_keeps_small_channels_that_per_tensor_scales_lose():
+    """Q and K rows and V channels shrunk by up to 2^-20: one scale for all of
+    V pushes its small channels below the format's smallest subnormal, while
+    a scale per 32-key block of each channel keeps them.  Both GPU results are
+    compared with the exact attention of the float32 inputs, each channel's
+    error in units of that channel's largest |V|."""
+    shape, scale = (1, 2, 512, 128), 1 / math.sqrt(128)
+    q, k, v = fa_inputs.draw_spread_f32(shape, 7, 20.0)
+    mx = fa_inputs.make_mx_inputs(shape, 7, 20.0)
+    o_true, _ = oracle.attn_fwd(q.astype(np.float64), k.astype(np.float64),
+                                v.astype(np.float64), scale, False)
+    o_mx, _ = run_mx(mx, scale, False)
+    (qc, sq), (kc, sk), (vc, sv) = (fa_inputs.quantize_e4m3fn(x) for x in (q, k, v))
+    o_pt = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(shape[:3], dtype=torch.float32, device="cuda")
+    fa.fa_fwd(dev(qc), dev(kc), dev(vc), o_pt, lse, scale, False, descale=(sq, sk, sv))
+    torch.cuda.synchronize()
+    v_chan = np.max(np.abs(v), axis=-2).astype(np.float64)
+
+    def chan_err(o):
+        return np.max(np.abs(o - o_true), axis=-2) / v_chan
+    e_mx, e_pt = chan_err(o_mx), chan_err(to_f64(o_pt))
+    say(f"per-channel error / channel scale: block scales max {e_mx.max():.3e}, "
+        f"per-tensor max {e_pt.max():.3e}")
+    assert e_mx.max() < 2e-2 and e_pt.max() > 2 * e_mx.max()

@@ -71,3 +71,70 @@ def test_workload_table():
     assert abs(c3.scale - 128 ** -0.5) < 1e-15
     assert w["fp32_fwdbwd_b1h1n128d64"].backward
     assert w["fp8_fwd_b1h32n16384d128"].dtype == "fp8"
+
+
+# --------------------------------------------------------------------------- #
+# Microscaled fp8 (e8m0 scale per 32 consecutive elements)
+# --------------------------------------------------------------------------- #
+def test_mx_scale_byte_closed_form():
+    # one block per row: the scale byte is floor(log2 amax) - 8 + 127
+    rows = [(1.0, 119), (448.0, 127), (3.0, 120), (0.75, 118), (2.0 ** 10, 129), (0.0, 0)]
+    x = np.zeros((len(rows), 32), np.float32)
+    for i, (amax, _) in enumerate(rows):
+        x[i, 5] = -amax
+    _, e = fa_inputs.quantize_mx_e4m3fn(x, -1)
+    assert e.shape == (len(rows), 1)
+    assert [int(v) for v in e[:, 0]] == [b for _, b in rows]
+    # and the decoder reads byte E as 2^(E - 127)
+    one = np.full((1, 32), 0x38, np.uint8)  # e4m3fn code of 1.0
+    for byte, value in ((127, 1.0), (128, 2.0), (120, 2.0 ** -7), (0, 2.0 ** -127)):
+        got = oracle.decode_mx_e4m3fn(one, np.array([[byte]], np.uint8), -1)
+        assert np.all(got == value)
+
+
+def test_mx_roundtrip_is_exact_on_representable_blocks():
+    # blocks of (small integer m) * 2^k with |m| <= 14 and amax 14 * 2^k: the
+    # scale is 2^(k - 5), every element is m * 32 <= 448 with at most four
+    # significant bits -- an e4m3 value -- so nothing rounds
+    rng = np.random.default_rng(5)
+    k = rng.integers(-20, 20, size=(6, 4, 1))
+    m = rng.integers(-14, 15, size=(6, 4, 32)).astype(np.float64)
+    m[..., 0] = 14.0
+    x = (m * np.exp2(k)).reshape(6, 128).astype(np.float32)
+    codes, e = fa_inputs.quantize_mx_e4m3fn(x, -1)
+    np.testing.assert_array_equal(oracle.decode_mx_e4m3fn(codes, e, -1), x.astype(np.float64))
+
+
+def test_mx_blocks_follow_the_axis():
+    # V is blocked along the sequence axis: changing one element moves only
+    # the scale of its own 32-row block of that column
+    x = np.ones((1, 1, 70, 8), np.float32)
+    _, e0 = fa_inputs.quantize_mx_e4m3fn(x, -2)
+    assert e0.shape == (1, 1, 3, 8)
+    x[0, 0, 40, 3] = 1000.0
+    _, e1 = fa_inputs.quantize_mx_e4m3fn(x, -2)
+    changed = np.argwhere(e1 != e0)
+    assert changed.tolist() == [[0, 0, 1, 3]]
+
+
+def test_mx_error_is_within_the_format_step():
+    x = np.random.default_rng(2).standard_normal((4, 256)).astype(np.float32)
+    x *= np.exp2(np.random.default_rng(3).uniform(-6, 6, size=(4, 1))).astype(np.float32)
+    codes, e = fa_inputs.quantize_mx_e4m3fn(x, -1)
+    y = oracle.decode_mx_e4m3fn(codes, e, -1)
+    scale = np.repeat(np.exp2(e.astype(np.float64) - 127), 32, axis=-1)
+    # e4m3 normal numbers carry 3 mantissa bits: RNE error <= 2^-4 relative;
+    # below 2^-6 (subnormal) the step is 2^-9, absolute, in units of the
+    # scale; and x / scale can reach up to 512, above the largest code 448,
+    # where the quantiser saturates (the OCP choice of the shared exponent)
+    bound = np.maximum.reduce([np.abs(x) * 2.0 ** -4, scale * 2.0 ** -10,
+                               np.abs(x) - 448.0 * scale])
+    assert np.all(np.abs(y) <= 448.0 * scale)
+    assert np.all(np.abs(y - x) <= bound)
+
+
+def test_make_mx_inputs_layout():
+    mx = fa_inputs.make_mx_inputs((1, 2, 70, 64), seed=3)
+    assert mx.q.shape == (1, 2, 70, 64) and mx.q.dtype == np.uint8
+    assert mx.qs.shape == mx.ks.shape == (1, 2, 70, 4) and mx.vs.shape == (1, 2, 3, 64)
+    assert np.all(mx.qs[..., 2:] == 127)
