@@ -36,15 +36,24 @@ EXTRA = ["bf16_causal_fwd_b2h32n8192d128", "bf16_fwd_b4h16n2048d64", "fp8_fwd_b1
 MX_EXTRA = ("mxfp8_fwd_b1h32n16384d128", (1, 32, 16384, 128))
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the HIP sources (name + bytes, sorted by name)."""
-    import glob
+# The sources each timed kernel is built from (with the build flags): a
+# counter figure stays valid while these files are unchanged.
+STAGE_SOURCES = {
+    "fwd": ["csrc/fwd_bf16.hip", "csrc/fa_device.h", "csrc/fa_kernels.h", "build.py"],
+    "delta": ["csrc/f32_kernels.hip", "csrc/fa_device.h", "csrc/fa_kernels.h", "build.py"],
+    "dkdv": ["csrc/bwd_bf16.hip", "csrc/fa_device.h", "csrc/fa_kernels.h", "build.py"],
+    "dq": ["csrc/bwd_bf16.hip", "csrc/fa_device.h", "csrc/fa_kernels.h", "build.py"],
+}
+
+
+def source_hash(stage: str) -> str:
+    """sha256 over the files a stage's kernel is built from (name + bytes)."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "exact_io_aware_11_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for rel in STAGE_SOURCES[stage]:
+        h.update(rel.encode())
+        with open(os.path.join(ROOT, "exact_io_aware_11_amd", rel), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -52,17 +61,20 @@ def kernel_source_hash() -> str:
 def measured_traffic(workload: str, stage: str):
     """HBM bytes per launch of `stage` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, scaled by a copy-kernel calibration),
-    or None if it was taken on other kernel sources or another workload."""
+    or None if it was taken on other sources of that kernel or another
+    workload."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != kernel_source_hash() or t.get("workload") != workload:
-        return None
     st = t.get("stages", {}).get(stage)
-    return None if st is None else st["bytes_per_launch"]
+    if t.get("workload") != workload or st is None or stage not in STAGE_SOURCES:
+        return None
+    if st.get("source_sha256") != source_hash(stage):
+        return None
+    return st["bytes_per_launch"]
 
 
 def log(*a):
