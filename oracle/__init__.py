@@ -14,10 +14,14 @@ eliminating IO", deep-learning-notes ch10.2; "Flash Attention V1/V2/V3" explaine
 
 * :func:`attn_fwd` / :func:`attn_fwd_rows` -- the definition of section 10.2.1
   (safe softmax with the row max, O = P V) with the 1/sqrt(d)-style scale of
-  section 10.2.3 as an argument; LSE = m + ln l.
+  section 10.2.3 as an argument; LSE = m + ln l.  Optional additive bias on
+  the scaled scores (the explainer's V2 section merges mask and bias into the
+  score stage): s = scale q.k + bias, -inf masks a key; a row with no finite
+  score gets O = 0 and LSE = -inf.
 * :func:`attn_bwd` -- the gradients of section 10.2.4 (dV = P^T dO,
   dP = dO V^T, dS = P o (dP - delta), dQ = dS K, dK = dS^T Q) with the scale
-  restored by the chain rule.
+  restored by the chain rule; the optional bias enters P as in the forward
+  (it is an input: no gradient is formed for it).
 * :func:`tiled_fwd` -- the tile update of section 10.2.2 (m~, P~, l~, alpha,
   beta, normalised O') in the FA1 loop order of section 10.2.5.
 * :func:`tiled_bwd` -- the recompute backward of section 10.2.4 from the saved
@@ -78,6 +82,12 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         lib.oracle_attn_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _L, _L, _L, _L,
                                         ctypes.c_double, ctypes.c_int, ctypes.c_int]
+        lib.oracle_attn_fwd_bias.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _L, _L, _L, _L,
+                                             ctypes.c_double, ctypes.c_int, ctypes.c_int]
+        lib.oracle_attn_fwd_rows_bias.argtypes = [_dp, _dp, _dp, _dp, _L, _L, ctypes.c_double,
+                                                  ctypes.c_int, _lp, _L, _dp, _dp, ctypes.c_int]
+        lib.oracle_attn_bwd_bias.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _L, _L,
+                                             _L, _L, ctypes.c_double, ctypes.c_int, ctypes.c_int]
         lib.oracle_attn_fwd_rows.argtypes = [_dp, _dp, _dp, _L, _L, ctypes.c_double,
                                              ctypes.c_int, _lp, _L, _dp, _dp, ctypes.c_int]
         lib.oracle_attn_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _L, _L, _L, _L,
@@ -91,7 +101,8 @@ def _load():
         lib.oracle_decode_e4m3fn.argtypes = [ctypes.POINTER(ctypes.c_ubyte), ctypes.c_double,
                                              _dp, _L]
         for name in ("oracle_attn_fwd", "oracle_attn_fwd_rows", "oracle_attn_bwd",
-                     "oracle_tiled_fwd", "oracle_tiled_bwd"):
+                     "oracle_attn_fwd_bias", "oracle_attn_fwd_rows_bias",
+                     "oracle_attn_bwd_bias", "oracle_tiled_fwd", "oracle_tiled_bwd"):
             getattr(lib, name).restype = ctypes.c_int
         lib.oracle_decode_bf16.restype = None
         lib.oracle_decode_e4m3fn.restype = None
@@ -125,8 +136,16 @@ def _check(rc: int, name: str):
         raise RuntimeError(f"{name} returned {rc}")
 
 
-def attn_fwd(q, k, v, scale: float, causal: bool, nthreads: int | None = None):
-    """Naive forward by definition.  Returns (O [B,H,N,d], LSE [B,H,N]) in float64."""
+def _bias4(bias, B, H, N):
+    """An additive bias broadcast to a contiguous float64 [B, H, N, N] array."""
+    return _f64(np.broadcast_to(np.asarray(bias, dtype=np.float64), (B, H, N, N)))
+
+
+def attn_fwd(q, k, v, scale: float, causal: bool, nthreads: int | None = None, bias=None):
+    """Naive forward by definition.  Returns (O [B,H,N,d], LSE [B,H,N]) in float64.
+
+    bias: None, or an array broadcastable to [B, H, N, N] added to the scaled
+    scores (-inf masks a key)."""
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = _shape4(q)
@@ -134,37 +153,52 @@ def attn_fwd(q, k, v, scale: float, causal: bool, nthreads: int | None = None):
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
     o = np.zeros_like(q)
     lse = np.zeros((B, H, N), dtype=np.float64)
-    _check(lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
-                               float(scale), int(bool(causal)),
-                               nthreads or default_threads()), "oracle_attn_fwd")
+    nt = nthreads or default_threads()
+    if bias is None:
+        rc = lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                 float(scale), int(bool(causal)), nt)
+    else:
+        b = _bias4(bias, B, H, N)
+        rc = lib.oracle_attn_fwd_bias(_ptr(q), _ptr(k), _ptr(v), _ptr(b), _ptr(o), _ptr(lse),
+                                      B, H, N, d, float(scale), int(bool(causal)), nt)
+    _check(rc, "oracle_attn_fwd")
     return o, lse
 
 
 def attn_fwd_rows(q_head, k_head, v_head, rows, scale: float, causal: bool,
-                  nthreads: int | None = None):
-    """Selected rows of ONE head ([N, d] inputs).  Returns (O rows [R, d], LSE rows [R])."""
+                  nthreads: int | None = None, bias_rows=None):
+    """Selected rows of ONE head ([N, d] inputs).  Returns (O rows [R, d], LSE rows [R]).
+
+    bias_rows: None, or the [R, N] bias of the selected rows."""
     lib = _load()
     q, k, v = _f64(q_head), _f64(k_head), _f64(v_head)
     N, d = q.shape
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     o = np.zeros((rows.size, d), dtype=np.float64)
     lse = np.zeros(rows.size, dtype=np.float64)
-    _check(lib.oracle_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), N, d, float(scale),
-                                    int(bool(causal)), rows.ctypes.data_as(_lp), rows.size,
-                                    _ptr(o), _ptr(lse), nthreads or default_threads()),
+    b = None if bias_rows is None else _f64(np.broadcast_to(bias_rows, (rows.size, N)))
+    _check(lib.oracle_attn_fwd_rows_bias(_ptr(q), _ptr(k), _ptr(v),
+                                         None if b is None else _ptr(b), N, d, float(scale),
+                                         int(bool(causal)), rows.ctypes.data_as(_lp), rows.size,
+                                         _ptr(o), _ptr(lse), nthreads or default_threads()),
            "oracle_attn_fwd_rows")
     return o, lse
 
 
-def attn_bwd(q, k, v, dout, scale: float, causal: bool, nthreads: int | None = None):
-    """Naive backward by definition.  Returns (dQ, dK, dV) in float64."""
+def attn_bwd(q, k, v, dout, scale: float, causal: bool, nthreads: int | None = None,
+             bias=None):
+    """Naive backward by definition.  Returns (dQ, dK, dV) in float64.
+
+    bias: as for attn_fwd (an input; no gradient is formed for it)."""
     lib = _load()
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, H, N, d = _shape4(q)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(q), np.zeros_like(q)
-    _check(lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
-                               _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
-                               nthreads or default_threads()), "oracle_attn_bwd")
+    b = None if bias is None else _bias4(bias, B, H, N)
+    _check(lib.oracle_attn_bwd_bias(_ptr(q), _ptr(k), _ptr(v), None if b is None else _ptr(b),
+                                    _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
+                                    float(scale), int(bool(causal)),
+                                    nthreads or default_threads()), "oracle_attn_bwd")
     return dq, dk, dv
 
 

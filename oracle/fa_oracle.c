@@ -28,6 +28,13 @@
  * N_q = N_k = N).  LSE_i = m_i + ln l_i in the natural log of the scaled
  * scores.
  *
+ * Bias and general masks (the explainer's V2 section: mask and bias are
+ * merged into the score computation): the *_bias functions add bias_ij to the
+ * scaled score, s_ij = scale q_i.k_j + bias_ij, before the softmax; a bias of
+ * -inf masks the key (exp(-inf - m) = 0).  A row whose visible scores are all
+ * -inf has an empty softmax: its output row is 0, its LSE is -inf (ln of an
+ * empty sum) and it contributes nothing to any gradient.
+ *
  * Layout: every tensor is a contiguous [B, H, N, d] array of doubles, and
  * LSE / delta are [B, H, N].  All sums are sequential double sums in index
  * order.  No blocking, fusion or reordering beyond what the definitions say.
@@ -130,19 +137,26 @@ static long visible_keys(long i, long N, int causal) { return causal ? i + 1 : N
 /* Forward, by definition (10.2.1), one query row at a time.           */
 /* ------------------------------------------------------------------ */
 
-/* One query row of one head: s_j = scale q.k_j, m = max s, l = sum exp(s - m),
- * P_j = exp(s_j - m) / l, o = sum_j P_j v_j, lse = m + ln l.
+/* One query row of one head: s_j = scale q.k_j (+ bias_i[j] when bias_i is
+ * given), m = max s, l = sum exp(s - m), P_j = exp(s_j - m) / l,
+ * o = sum_j P_j v_j, lse = m + ln l; an all -inf row gives o = 0, lse = -inf.
  * s is caller scratch of N doubles. */
-static void fwd_row(const double *q_i, const double *K, const double *V, long N, long d,
-                    double scale, long n_vis, double *s, double *o_i, double *lse_i) {
+static void fwd_row(const double *q_i, const double *K, const double *V, const double *bias_i,
+                    long N, long d, double scale, long n_vis, double *s, double *o_i,
+                    double *lse_i) {
   long j, c;
   double m = -INFINITY, l = 0.0;
   for (j = 0; j < n_vis; ++j) {
     s[j] = scale * dot(q_i, K + j * d, d);
+    if (bias_i) s[j] += bias_i[j];
     if (s[j] > m) m = s[j];
   }
-  for (j = 0; j < n_vis; ++j) l += exp(s[j] - m);
   for (c = 0; c < d; ++c) o_i[c] = 0.0;
+  if (m == -INFINITY) { /* no visible key with a finite score */
+    *lse_i = -INFINITY;
+    return;
+  }
+  for (j = 0; j < n_vis; ++j) l += exp(s[j] - m);
   for (j = 0; j < n_vis; ++j) {
     const double p = exp(s[j] - m) / l;
     const double *v_j = V + j * d;
@@ -154,6 +168,7 @@ static void fwd_row(const double *q_i, const double *K, const double *V, long N,
 
 typedef struct {
   const double *q, *k, *v;
+  const double *bias; /* [B, H, N, N] or NULL */
   double *o, *lse;
   long N, d, chunk, chunks_per_head;
   double scale;
@@ -170,19 +185,22 @@ static void fwd_item(void *p, long item, int tid) {
   long i;
   (void)tid;
   for (i = r0; i < r1; ++i)
-    fwd_row(c->q + bh * hd + i * c->d, c->k + bh * hd, c->v + bh * hd, c->N, c->d, c->scale,
+    fwd_row(c->q + bh * hd + i * c->d, c->k + bh * hd, c->v + bh * hd,
+            c->bias ? c->bias + (bh * c->N + i) * c->N : NULL, c->N, c->d, c->scale,
             visible_keys(i, c->N, c->causal), s, c->o + bh * hd + i * c->d,
             c->lse + bh * c->N + i);
   free(s);
 }
 
-/* Full forward over [B,H,N,d].  Returns 0, or -1 on bad sizes. */
-int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o, double *lse,
-                    long B, long H, long N, long d, double scale, int causal, int nthreads) {
+/* Full forward over [B,H,N,d], with an optional [B,H,N,N] additive bias on the
+ * scaled scores (NULL: none).  Returns 0, or -1 on bad sizes. */
+int oracle_attn_fwd_bias(const double *q, const double *k, const double *v, const double *bias,
+                         double *o, double *lse, long B, long H, long N, long d, double scale,
+                         int causal, int nthreads) {
   fwd_ctx_t c;
   if (B < 0 || H < 0 || N < 0 || d < 1) return -1;
   if (B * H * N == 0) return 0;
-  c.q = q; c.k = k; c.v = v; c.o = o; c.lse = lse;
+  c.q = q; c.k = k; c.v = v; c.bias = bias; c.o = o; c.lse = lse;
   c.N = N; c.d = d; c.scale = scale; c.causal = causal;
   c.chunk = 64;
   c.chunks_per_head = (N + c.chunk - 1) / c.chunk;
@@ -190,9 +208,16 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o
   return 0;
 }
 
+/* Full forward over [B,H,N,d] without a bias. */
+int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o, double *lse,
+                    long B, long H, long N, long d, double scale, int causal, int nthreads) {
+  return oracle_attn_fwd_bias(q, k, v, NULL, o, lse, B, H, N, d, scale, causal, nthreads);
+}
+
 typedef struct {
   const double *q, *k, *v;
   const long *rows;
+  const double *bias; /* [n_rows, N] or NULL */
   double *o, *lse;
   long N, d;
   double scale;
@@ -204,26 +229,36 @@ static void rows_item(void *p, long item, int tid) {
   const long i = c->rows[item];
   double *s = (double *)malloc(sizeof(double) * (size_t)c->N);
   (void)tid;
-  fwd_row(c->q + i * c->d, c->k, c->v, c->N, c->d, c->scale, visible_keys(i, c->N, c->causal),
-          s, c->o + item * c->d, c->lse + item);
+  fwd_row(c->q + i * c->d, c->k, c->v, c->bias ? c->bias + item * c->N : NULL, c->N, c->d,
+          c->scale, visible_keys(i, c->N, c->causal), s, c->o + item * c->d, c->lse + item);
   free(s);
 }
 
 /* Selected query rows of ONE head: q, k, v are [N, d]; rows[r] in [0, N);
+ * bias_rows (or NULL) is [n_rows, N], the bias of each selected row;
  * o_rows is [n_rows, d], lse_rows is [n_rows].  Same arithmetic as
- * oracle_attn_fwd, for sampled checks at sizes where the full run is slow. */
-int oracle_attn_fwd_rows(const double *q, const double *k, const double *v, long N, long d,
-                         double scale, int causal, const long *rows, long n_rows, double *o_rows,
-                         double *lse_rows, int nthreads) {
+ * oracle_attn_fwd_bias, for sampled checks at sizes where the full run is
+ * slow. */
+int oracle_attn_fwd_rows_bias(const double *q, const double *k, const double *v,
+                              const double *bias_rows, long N, long d, double scale, int causal,
+                              const long *rows, long n_rows, double *o_rows, double *lse_rows,
+                              int nthreads) {
   rows_ctx_t c;
   long r;
   if (N < 1 || d < 1 || n_rows < 0) return -1;
   for (r = 0; r < n_rows; ++r)
     if (rows[r] < 0 || rows[r] >= N) return -1;
-  c.q = q; c.k = k; c.v = v; c.rows = rows; c.o = o_rows; c.lse = lse_rows;
+  c.q = q; c.k = k; c.v = v; c.rows = rows; c.bias = bias_rows; c.o = o_rows; c.lse = lse_rows;
   c.N = N; c.d = d; c.scale = scale; c.causal = causal;
   run_pool(rows_item, &c, n_rows, nthreads);
   return 0;
+}
+
+int oracle_attn_fwd_rows(const double *q, const double *k, const double *v, long N, long d,
+                         double scale, int causal, const long *rows, long n_rows, double *o_rows,
+                         double *lse_rows, int nthreads) {
+  return oracle_attn_fwd_rows_bias(q, k, v, NULL, N, d, scale, causal, rows, n_rows, o_rows,
+                                   lse_rows, nthreads);
 }
 
 /* ------------------------------------------------------------------ */
@@ -242,6 +277,7 @@ int oracle_attn_fwd_rows(const double *q, const double *k, const double *v, long
 
 typedef struct {
   const double *q, *k, *v, *dout;
+  const double *bias; /* [B, H, N, N] or NULL */
   double *dq;
   double *dk_part, *dv_part; /* [nthreads][N][d] for the current head */
   long N, d, chunk, n_chunks;
@@ -266,19 +302,22 @@ static void bwd_item(void *p, long item, int tid) {
   for (i = r0; i < r1; ++i) {
     const long n_vis = visible_keys(i, N, c->causal);
     const double *q_i = Q + i * d, *do_i = dO + i * d;
+    const double *bias_i = c->bias ? c->bias + (c->bh * N + i) * N : NULL;
     double m = -INFINITY, l = 0.0, delta = 0.0;
     double *dq_i = dQ + i * d;
     for (j = 0; j < n_vis; ++j) {
       s[j] = c->scale * dot(q_i, K + j * d, d);
+      if (bias_i) s[j] += bias_i[j];
       if (s[j] > m) m = s[j];
     }
+    for (cc = 0; cc < d; ++cc) dq_i[cc] = 0.0;
+    if (m == -INFINITY) continue; /* empty softmax: P = 0, no gradient */
     for (j = 0; j < n_vis; ++j) l += exp(s[j] - m);
     for (j = 0; j < n_vis; ++j) {
       pr[j] = exp(s[j] - m) / l;
       dp[j] = dot(do_i, V + j * d, d);
       delta += pr[j] * dp[j];
     }
-    for (cc = 0; cc < d; ++cc) dq_i[cc] = 0.0;
     for (j = 0; j < n_vis; ++j) {
       const double ds = pr[j] * (dp[j] - delta);
       const double *k_j = K + j * d;
@@ -295,11 +334,12 @@ static void bwd_item(void *p, long item, int tid) {
   free(dp);
 }
 
-/* Full backward over [B,H,N,d]: dq, dk, dv out.  Returns 0, -1 on bad sizes,
- * -2 if scratch could not be allocated. */
-int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
-                    double *dq, double *dk, double *dv, long B, long H, long N, long d,
-                    double scale, int causal, int nthreads) {
+/* Full backward over [B,H,N,d] with an optional [B,H,N,N] bias (NULL: none;
+ * the bias is an input, no gradient is formed for it): dq, dk, dv out.
+ * Returns 0, -1 on bad sizes, -2 if scratch could not be allocated. */
+int oracle_attn_bwd_bias(const double *q, const double *k, const double *v, const double *bias,
+                         const double *dout, double *dq, double *dk, double *dv, long B, long H,
+                         long N, long d, double scale, int causal, int nthreads) {
   bwd_ctx_t c;
   long bh, t, x;
   int nt;
@@ -317,7 +357,7 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
     free(c.dv_part);
     return -2;
   }
-  c.q = q; c.k = k; c.v = v; c.dout = dout; c.dq = dq;
+  c.q = q; c.k = k; c.v = v; c.bias = bias; c.dout = dout; c.dq = dq;
   c.N = N; c.d = d; c.scale = scale; c.causal = causal;
   for (bh = 0; bh < B * H; ++bh) {
     c.bh = bh;
@@ -337,6 +377,13 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
   free(c.dk_part);
   free(c.dv_part);
   return 0;
+}
+
+int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
+                    double *dq, double *dk, double *dv, long B, long H, long N, long d,
+                    double scale, int causal, int nthreads) {
+  return oracle_attn_bwd_bias(q, k, v, NULL, dout, dq, dk, dv, B, H, N, d, scale, causal,
+                              nthreads);
 }
 
 /* ------------------------------------------------------------------ */
