@@ -7,6 +7,8 @@ C names:
 
 * :func:`fa_fwd` -- O and LSE from Q, K, V
 * :func:`fa_fwd_mxfp8` -- the same on fp8 codes with e8m0 block scales
+* :func:`fa_fwd_bias`, :func:`fa_bwd_bias` -- forward and backward with an
+  additive bias (and masks, as -inf) on the scaled scores
 * :func:`fa_bwd` -- dQ, dK, dV from Q, K, V, O, dO, LSE (and a workspace)
 * :func:`fa_bwd_delta`, :func:`fa_bwd_dkdv`, :func:`fa_bwd_dq` -- fa_bwd's three stages
 * :func:`fa_bwd_workspace_size`, :func:`fa_status_string`
@@ -18,13 +20,14 @@ from __future__ import annotations
 
 from ._lib import (FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_FP32,
                    FA_FP8_E4M3, FA_OK, FAError, lib)
-from .api import (dtype_code, fa_bwd, fa_bwd_delta, fa_bwd_dkdv, fa_bwd_dq,
-                  fa_bwd_workspace_size, fa_fwd, fa_fwd_mxfp8, fa_status_string, flops_bwd,
-                  flops_fwd)
+from .api import (dtype_code, fa_bwd, fa_bwd_bias, fa_bwd_delta, fa_bwd_dkdv, fa_bwd_dq,
+                  fa_bwd_workspace_size, fa_fwd, fa_fwd_bias, fa_fwd_mxfp8, fa_status_string,
+                  flops_bwd, flops_fwd)
 
 __all__ = [
     "FA_FP32", "FA_BF16", "FA_FP8_E4M3", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",
-    "FA_ERR_HIP", "FAError", "lib", "fa_fwd", "fa_fwd_mxfp8", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv",
+    "FA_ERR_HIP", "FAError", "lib", "fa_fwd", "fa_fwd_bias", "fa_fwd_mxfp8", "fa_bwd",
+    "fa_bwd_bias", "fa_bwd_delta", "fa_bwd_dkdv",
     "fa_bwd_dq", "fa_bwd_workspace_size",
     "fa_status_string", "dtype_code", "flops_fwd", "flops_bwd",
 ]

@@ -11,12 +11,17 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 # The entry points include/fa.h declares, with their ctypes signatures.
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_ll = ctypes.c_longlong
 SIGNATURES = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _f, _f, _f, _vp]),
     "fa_fwd_mxfp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]),
     "fa_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _f,
                     _i, _i, _vp]),
+    "fa_fwd_bias": (_i, [_vp, _vp, _vp, _vp, _ll, _ll, _ll, _vp, _vp, _i, _i, _i, _i, _f, _i,
+                         _i, _vp]),
+    "fa_bwd_bias": (_i, [_vp, _vp, _vp, _vp, _ll, _ll, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                         _sz, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
 }
 for _stage in ("fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq"):

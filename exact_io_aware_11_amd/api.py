@@ -102,6 +102,70 @@ def fa_fwd_mxfp8(q, k, v, q_scale, k_scale, v_scale, o, lse, scale: float, causa
         raise FAError(st, "fa_fwd_mxfp8: " + fa_status_string(st))
 
 
+def _bias_view(bias, B, H, N):
+    """A float32 bias tensor broadcast to [B, H, N, N]: (pointer, strides b, h, q)."""
+    import torch
+
+    if bias.dtype != torch.float32:
+        raise TypeError("bias must be float32")
+    if bias.dim() != 4:
+        raise ValueError("bias must be 4-D, broadcastable to [B, H, N, N]")
+    b = bias.expand(B, H, N, N)
+    if b.stride(3) != 1:
+        raise ValueError("bias must have unit stride along the key dimension")
+    return b.data_ptr(), b.stride(0), b.stride(1), b.stride(2)
+
+
+def fa_fwd_bias(q, k, v, bias, o, lse, scale: float, causal: bool, stream=None):
+    """Enqueue the forward pass with an additive float32 bias on the scaled
+    scores (-inf masks a key).  bias is a 4-D tensor broadcastable to
+    [B, H, N, N] whose strides (in elements) are multiples of 4 and whose last
+    stride is 1 (a view of a row-pitched buffer works).  Writes o and lse;
+    rows with no finite score get o = 0 and lse = -inf."""
+    import torch
+
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_like(name, t, (B, H, N, d))
+    _check_like("lse", lse, (B, H, N))
+    code = dtype_code(q)
+    if code == FA_FP8_E4M3:
+        raise FAError(2, "fa_fwd_bias: float32 or bfloat16 inputs")
+    _check_dtypes(code, (("k", k), ("v", v)), (("o", o),))
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    bp, sb, sh, sq = _bias_view(bias, B, H, N)
+    st = lib.fa_fwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), bp, sb, sh, sq, o.data_ptr(),
+                         lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), code,
+                         _stream_handle(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_bias: " + fa_status_string(st))
+
+
+def fa_bwd_bias(q, k, v, bias, o, dout, lse, dq, dk, dv, workspace, scale: float, causal: bool,
+                stream=None):
+    """Enqueue the backward pass with the bias of fa_fwd_bias (an input: no
+    gradient is formed for it).  Writes dq, dk, dv."""
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _check_like(name, t, (B, H, N, d))
+    _check_like("lse", lse, (B, H, N))
+    code = dtype_code(q)
+    if code == FA_FP8_E4M3:
+        raise FAError(2, "fa_bwd_bias: the backward takes float32 or bfloat16 tensors")
+    _check_dtypes(code, (("k", k), ("v", v), ("o", o), ("dout", dout)),
+                  (("dq", dq), ("dk", dk), ("dv", dv)))
+    bp, sb, sh, sq = _bias_view(bias, B, H, N)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_bwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), bp, sb, sh, sq, o.data_ptr(),
+                         dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                         dv.data_ptr(), workspace.data_ptr(), nbytes, B, H, N, d, float(scale),
+                         int(bool(causal)), code, _stream_handle(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_bias: " + fa_status_string(st))
+
+
 def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(lib.fa_bwd_workspace_size(B, H, N, d))
 
@@ -168,6 +232,7 @@ def flops_bwd(B, H, N, d, causal) -> float:
     return f / 2 if causal else f
 
 
-__all__ = ["FA_FP32", "FA_BF16", "FA_FP8_E4M3", "dtype_code", "fa_fwd", "fa_bwd",
+__all__ = ["FA_FP32", "FA_BF16", "FA_FP8_E4M3", "dtype_code", "fa_fwd", "fa_fwd_bias",
+           "fa_fwd_mxfp8", "fa_bwd", "fa_bwd_bias",
            "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_bwd_workspace_size", "fa_status_string", "flops_fwd", "flops_bwd"]

@@ -22,6 +22,11 @@
 //    the transposing LDS read.
 // Recomputing S and dP in the dQ pass costs two extra matrix products over
 // the five the method needs; it keeps every output written exactly once.
+//
+// Optional additive bias (explainer V2 section: mask and bias merged into the
+// score stage): P = exp(scale S + bias - LSE); each tile's bias values are
+// loaded during the previous tile; rows whose LSE is -inf (no finite score in
+// the forward) get P = 0.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -29,13 +34,13 @@
 
 namespace fa {
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int N, uint32_t n_kblk, uint32_t total, float scale,
-    float scale_log2) {
+    float scale_log2, Bias bias) {
   constexpr int BN = 128, BM = 64, TILE = BM * D;
   constexpr int LPW = TILE * 2 / 1024 / 4;  // 1 KiB direct loads per wave per tile
   constexpr int NT = D / 16, NCB = D / 32;
@@ -61,6 +66,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 
   const int k0 = (int)kblk * BN + wave * 32;
   const int kcol = k0 + r32;  // this lane's key (C-layout column)
+
+  // Additive bias: element i of query half qb of a tile at qbase is
+  // (row qbase + 32 qb + 8 (i / 4) + 4 g + i % 4, key kcol); the lane part of
+  // the byte offset is fixed, the row part wave-uniform (scalar offset).
+  // Reads past the slice return zeros; key columns past N are never written.
+  [[maybe_unused]] const auto brs = BIAS ? bias_rsrc(bias, bh) : make_rsrc(nullptr, 0);
+  [[maybe_unused]] const uint32_t bvoff =
+      BIAS ? (uint32_t)(((long long)min(kcol, N - 1) + 4LL * g * bias.sq) * 4) : 0u;
+  [[maybe_unused]] float bsv[2][2][16];  // [buffer][query half][element]
+  auto load_bias = [&](auto bufc, int qb, int i, int qbase) {
+    constexpr int BB = decltype(bufc)::value;
+    const uint32_t row = (uint32_t)(qbase + 32 * qb + 8 * (i >> 2) + (i & 3));
+    bsv[BB][qb][i] = buffer_load_f32(brs, bvoff, (uint32_t)(row * bias.sq * 4));
+  };
 
   // K and V rows as the B operands of S = Q K^T and dP = dO V^T.
   bf16x8 kf[NT], vf[NT];
@@ -142,9 +161,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // past N (K, V rows zero) only reach dK/dV columns that are never written.
   auto store_stats = [&](int it, int buf) {
     const int q = it * BM + (tid & (BM - 1));
+    // (with a bias, an LSE of -inf -- a row with no finite score -- becomes
+    // +inf too: its P is 0)
+    const bool live = q < N && (!BIAS || sreg != -__builtin_inff());
     if (tid < 2 * BM)
       lst[buf][tid / BM][tid & (BM - 1)] =
-          tid < BM ? (q < N ? sreg * kLog2e : __builtin_inff()) : (q < N ? sreg : 0.f);
+          tid < BM ? (live ? sreg * kLog2e : __builtin_inff()) : (q < N ? sreg : 0.f);
   };
 
   f32x16 adk[NCB], adv[NCB];
@@ -212,7 +234,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     // softmax-backward arithmetic of element i (0..15) of half qb
     auto soft_elem = [&](int qb, int i) {
       const float l2 = l2v[i >> 2][i & 3], dl = dlv[i >> 2][i & 3];
-      float p = exp2_fast(fmaf(s[qb][i], scale_log2, -l2));
+      float arg = -l2;
+      if constexpr (BIAS) arg = fmaf(bsv[BUF][qb][i], kLog2e, arg);
+      float p = exp2_fast(fmaf(s[qb][i], scale_log2, arg));
       if constexpr (masked) {  // row of element i: qbase + 32 qb + 4 g + 8 (i / 4) + i % 4
         if (kcol - (qbase + 32 * qb + 4 * g) > 8 * (i >> 2) + (i & 3)) p = 0.f;
       }
@@ -264,7 +288,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       for (int i = k * 16 / NB; i < (k + 1) * 16 / NB; ++i) soft_elem(1, i);
       stage_at(2 * NA + k);
     });
-    stream(true, 1, NB, none);
+    if constexpr (BIAS) {  // the next tile's bias, two or four loads per product
+      stream(true, 1, NB, [&](int k) {
+#pragma unroll
+        for (int e = k * 32 / NB; e < (k + 1) * 32 / NB; ++e)
+          load_bias(std::integral_constant<int, BUF ^ 1>{}, e >> 4, e & 15, qbase + BM);
+      });
+    } else {
+      stream(true, 1, NB, none);
+    }
   };
 
   // Two-stage pipeline over query tiles: tile it+1 streams into the other
@@ -286,6 +318,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   stage(it0, B0{});
   load_stats(it0);
   store_stats(it0, 0);
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) load_bias(B0{}, e >> 4, e & 15, it0 * BM);
+  }
   int it = it0;
   if (CAUSAL) {  // tiles it0 and it0 + 1 hold every (key > query) pair of the block
     // (it0 + 1 may lie past the end: its rows are all masked by the +inf LSE)
@@ -318,12 +354,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
+template <int D, bool CAUSAL, bool BIAS>
+__global__ __launch_bounds__(256, BIAS ? 1 : 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
-    int N, uint32_t n_qblk, uint32_t total, float scale, float scale_log2) {
+    int N, uint32_t n_qblk, uint32_t total, float scale, float scale_log2, Bias bias) {
   constexpr int BM = 128, BN = 64, TILE = BN * D;
   constexpr int LPW = TILE * 2 / 1024 / 4;  // 1 KiB direct loads per wave per tile and tensor
   constexpr int NT = D / 16, NCB = D / 32;
@@ -366,9 +402,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
       of[t] = bf16x8{};
     }
   }
-  // One query per lane column: LSE and delta are per-lane scalars.
-  const float lse2 = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  // One query per lane column: LSE and delta are per-lane scalars.  (With a
+  // bias, rows past N and rows with LSE = -inf -- no finite score -- take
+  // +inf, so that their P is exactly 0 whatever the bias there.)
+  float lse2 = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  if constexpr (BIAS) lse2 = (qrow < N && lse2 != -__builtin_inff()) ? lse2 : __builtin_inff();
   const float del = qrow < N ? Delta[(size_t)bh * N + qrow] : 0.f;
+  // Additive bias of this lane's query row: as in the forward, element i of
+  // key half b of a tile at key0 is key key0 + 32 b + 8 (i / 4) + 4 g + i % 4,
+  // load x = 4 b + i / 4 of 16 bytes, component i % 4.
+  [[maybe_unused]] const auto brs = BIAS ? bias_rsrc(bias, bh) : make_rsrc(nullptr, 0);
+  [[maybe_unused]] const uint32_t bvoff =
+      BIAS ? (uint32_t)((long long)min(qrow, N - 1) * bias.sq * 4 + 16 * g) : 0u;
+  [[maybe_unused]] f32x4 bv[2][8];  // [buffer][load]
+  auto load_bias = [&](auto bufc, int x, int key0) {
+    constexpr int BB = decltype(bufc)::value;
+    bv[BB][x] = buffer_load_f32x4(brs, bvoff + 128 * (x >> 2) + 32 * (x & 3), (uint32_t)key0 * 4u);
+  };
 
   // K / V rows as A operands: row r32 (+32 b), chunk 2t + g.
   int koff[NT];
@@ -407,8 +457,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 
   const int kv_end = CAUSAL ? min(N, (int)qblk * BM + BM) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
-  // Tiles [0, j_full) are visible to every query of the block.
-  const int j_full = CAUSAL ? (int)qblk * (BM / BN) : n_tiles;
+  // Tiles [0, j_full) are visible to every query of the block.  With a bias
+  // a ragged last tile is masked too: its keys past N read a bias from beyond
+  // the row, which must not reach an exp.
+  const int j_full = BIAS ? min(CAUSAL ? (int)qblk * (BM / BN) : n_tiles, N / BN)
+                          : (CAUSAL ? (int)qblk * (BM / BN) : n_tiles);
 
   f32x16 adq[NCB];
 #pragma unroll
@@ -427,7 +480,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   bf16x8 db[2][2];
   auto tile = [&](auto bufc, auto maskc, int j) {
     constexpr int BUF = decltype(bufc)::value;
-    constexpr bool masked = CAUSAL && decltype(maskc)::value;
+    constexpr bool masked = (CAUSAL || BIAS) && decltype(maskc)::value;
     using BN1 = std::integral_constant<int, BUF ^ 1>;
     const uint16_t* Kt = ktile(bufc);
     const uint16_t* Vt = vtile(bufc);
@@ -454,9 +507,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
       adq[cb] = mfma_bf16(a, db[b][h], adq[cb]);
     };
     auto soft_elem = [&](int b, int i) {  // key of element i: key0 + 32 b + 8 (i / 4) + 4 g + i % 4
-      float p = exp2_fast(fmaf(s[b][i], scale_log2, -lse2));
+      float arg = -lse2;
+      if constexpr (BIAS) arg = fmaf(bv[BUF][4 * b + (i >> 2)][i & 3], kLog2e, arg);
+      float p = exp2_fast(fmaf(s[b][i], scale_log2, arg));
       if constexpr (masked) {
-        if (key0 + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3) > qrow) p = 0.f;
+        const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3);
+        if ((CAUSAL && key > qrow) || (BIAS && key >= N)) p = 0.f;
       }
       dp[b][i] = p * (dp[b][i] - del);
       if ((i & 7) == 7) db[b][i >> 3] = to_bf16x8(dp[b], i - 7);
@@ -491,7 +547,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
       for (int i = k * 16 / NB; i < (k + 1) * 16 / NB; ++i) soft_elem(1, i);
       stage_at(2 * NA + k);
     });
-    stream(true, 1, NB, [](int) {});
+    if constexpr (BIAS) {  // the next tile's bias
+      stream(true, 1, NB, [&](int k) {
+#pragma unroll
+        for (int x = k * 8 / NB; x < (k + 1) * 8 / NB; ++x) load_bias(BN1{}, x, key0 + BN);
+      });
+    } else {
+      stream(true, 1, NB, [](int) {});
+    }
   };
 
   auto step = [&](auto bufc, auto maskc, int j) {
@@ -505,6 +568,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const auto vr = tile_rsrc(Vh, 0);
 #pragma unroll
     for (int L = 0; L < 2 * LPW; ++L) stage_one(kr, vr, B0{}, L);
+  }
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) load_bias(B0{}, x, 0);
   }
   int j = 0;
   for (; j + 2 <= j_full; j += 2) {
@@ -531,36 +598,45 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS>
 static hipError_t dkdv_bf16_t(const BwdArgs& a) {
   const uint32_t n_kblk = (uint32_t)((a.N + 127) / 128);
   const uint32_t total = (uint32_t)(a.BH * n_kblk);
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, BIAS>), dim3(total), dim3(256), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     a.N, n_kblk, total, a.scale, a.scale * kLog2e);
+                     a.N, n_kblk, total, a.scale, a.scale * kLog2e, a.bias);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool BIAS>
+static hipError_t dq_bf16_t(const BwdArgs& a) {
+  const uint32_t n_qblk = (uint32_t)((a.N + 127) / 128);
+  const uint32_t total = (uint32_t)(a.BH * n_qblk);
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, BIAS>), dim3(total), dim3(256), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.N, n_qblk,
+                     total, a.scale, a.scale * kLog2e, a.bias);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
-static hipError_t dq_bf16_t(const BwdArgs& a) {
-  const uint32_t n_qblk = (uint32_t)((a.N + 127) / 128);
-  const uint32_t total = (uint32_t)(a.BH * n_qblk);
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.N, n_qblk,
-                     total, a.scale, a.scale * kLog2e);
-  return hipGetLastError();
+static hipError_t dkdv_bf16_b(const BwdArgs& a) {
+  return a.bias.p ? dkdv_bf16_t<D, CAUSAL, true>(a) : dkdv_bf16_t<D, CAUSAL, false>(a);
+}
+template <int D, bool CAUSAL>
+static hipError_t dq_bf16_b(const BwdArgs& a) {
+  return a.bias.p ? dq_bf16_t<D, CAUSAL, true>(a) : dq_bf16_t<D, CAUSAL, false>(a);
 }
 
 hipError_t launch_dkdv_bf16(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? dkdv_bf16_t<64, true>(a) : dkdv_bf16_t<64, false>(a);
-  return a.causal ? dkdv_bf16_t<128, true>(a) : dkdv_bf16_t<128, false>(a);
+  if (a.d == 64) return a.causal ? dkdv_bf16_b<64, true>(a) : dkdv_bf16_b<64, false>(a);
+  return a.causal ? dkdv_bf16_b<128, true>(a) : dkdv_bf16_b<128, false>(a);
 }
 
 hipError_t launch_dq_bf16(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? dq_bf16_t<64, true>(a) : dq_bf16_t<64, false>(a);
-  return a.causal ? dq_bf16_t<128, true>(a) : dq_bf16_t<128, false>(a);
+  if (a.d == 64) return a.causal ? dq_bf16_b<64, true>(a) : dq_bf16_b<64, false>(a);
+  return a.causal ? dq_bf16_b<128, true>(a) : dq_bf16_b<128, false>(a);
 }
 
 }  // namespace fa

@@ -14,6 +14,11 @@
 // peak on the vector ALUs as on the matrix cores, so they are plain
 // LDS-tiled FMA kernels with exact expf/logf.  One workgroup of 256 threads
 // per (batch, head, 32-row block); 8 threads share a row.
+//
+// Optional additive bias on the scaled scores (explainer V2 section: mask and
+// bias merged into the score stage), read straight from global memory; -inf
+// masks a key, a row with no finite score gets O = 0 and LSE = -inf, and the
+// backward gives such rows (LSE = -inf) P = 0.
 #include <math.h>
 
 #include "fa_device.h"
@@ -48,6 +53,13 @@ __device__ __forceinline__ void load_rows(float (*dst)[LD], const float* src, in
   }
 }
 
+// Row `row` of the (b, h) slice of a bias, or null.
+__device__ __forceinline__ const float* bias_row(const Bias& b, size_t bh, int row) {
+  if (!b.p) return nullptr;
+  const size_t bi = bh / (size_t)b.H, hi = bh - bi * (size_t)b.H;
+  return b.p + (long long)bi * b.sb + (long long)hi * b.sh + (long long)row * b.sq;
+}
+
 }  // namespace
 
 template <int D, bool CAUSAL>
@@ -55,7 +67,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ K,
                                                       const float* __restrict__ V,
                                                       float* __restrict__ O,
-                                                      float* __restrict__ LSE, int N, float scale) {
+                                                      float* __restrict__ LSE, int N, float scale,
+                                                      Bias bias) {
   constexpr int DS = D / 8;
   __shared__ float Qs[kBR][D + 1], Ks[kBC][D + 1], Vs[kBC][D], Ps[kBR][kBC + 1];
   const int tid = threadIdx.x, r = tid >> 3, sub = tid & 7;
@@ -64,6 +77,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   const int q0 = (int)(blockIdx.x - bh * nq) * kBR, qrow = q0 + r;
   const size_t head = bh * (size_t)N * D;
   load_rows<D, D + 1>(Qs, Q + head, q0, kBR, N);
+  const float* brow = qrow < N ? bias_row(bias, bh, qrow) : nullptr;
   float acc[DS];
 #pragma unroll
   for (int x = 0; x < DS; ++x) acc[x] = 0.f;
@@ -80,16 +94,18 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
       const int c = sub + 8 * cc, key = k0 + c;
       float dot = 0.f;
       for (int x = 0; x < D; ++x) dot = fmaf(Qs[r][x], Ks[c][x], dot);
-      s[cc] = (key < N && (!CAUSAL || key <= qrow)) ? dot * scale : -INFINITY;
+      const bool vis = key < N && (!CAUSAL || key <= qrow);
+      s[cc] = vis ? dot * scale + (brow ? brow[key] : 0.f) : -INFINITY;
       mt = fmaxf(mt, s[cc]);
     }
     mt = group8_max(mt);
     const float m_new = fmaxf(m, mt);
-    const float alpha = expf(m - m_new);
+    // (m_new = -inf: no finite score yet; every p is 0 and nothing rescales)
+    const float alpha = m_new == -INFINITY ? 1.f : expf(m - m_new);
     float rs = 0.f;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const float p = expf(s[cc] - m_new);
+      const float p = m_new == -INFINITY ? 0.f : expf(s[cc] - m_new);
       Ps[r][sub + 8 * cc] = p;
       rs += p;
     }
@@ -108,8 +124,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   if (qrow < N) {
     float* Orow = O + head + (size_t)qrow * D + sub * DS;
 #pragma unroll
-    for (int x = 0; x < DS; ++x) Orow[x] = acc[x] / l;
-    if (sub == 0) LSE[bh * N + qrow] = m + logf(l);
+    for (int x = 0; x < DS; ++x) Orow[x] = l > 0.f ? acc[x] / l : 0.f;
+    if (sub == 0) LSE[bh * N + qrow] = l > 0.f ? m + logf(l) : -INFINITY;
   }
 }
 
@@ -117,7 +133,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    float* __restrict__ dK, float* __restrict__ dV, int N, float scale) {
+    float* __restrict__ dK, float* __restrict__ dV, int N, float scale, Bias bias) {
   constexpr int DS = D / 8;
   __shared__ float Ks[kBC][D + 1], Vs[kBC][D + 1], Qs[kBR][D + 1], dOs[kBR][D + 1];
   __shared__ float Ps[kBR][kBC + 1], dSs[kBR][kBC + 1], lse_s[kBR], del_s[kBR];
@@ -143,6 +159,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(
     }
     __syncthreads();
     const int q = q0 + r;
+    const float* brow = q < N ? bias_row(bias, bh, q) : nullptr;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const int c = sub + 8 * cc, key = k0 + c;
@@ -151,8 +168,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(
         sd = fmaf(Qs[r][x], Ks[c][x], sd);
         dpd = fmaf(dOs[r][x], Vs[c][x], dpd);
       }
-      const bool valid = key < N && q < N && (!CAUSAL || key <= q);
-      const float p = valid ? expf(sd * scale - lse_s[r]) : 0.f;
+      // (LSE = -inf: a row with no finite score, P = 0)
+      const bool valid = key < N && q < N && (!CAUSAL || key <= q) && lse_s[r] != -INFINITY;
+      const float p = valid ? expf(sd * scale + (brow ? brow[key] : 0.f) - lse_s[r]) : 0.f;
       Ps[r][c] = p;
       dSs[r][c] = p * (dpd - del_s[r]);
     }
@@ -184,7 +202,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    float* __restrict__ dQ, int N, float scale) {
+    float* __restrict__ dQ, int N, float scale, Bias bias) {
   constexpr int DS = D / 8;
   __shared__ float Qs[kBR][D + 1], dOs[kBR][D + 1], Ks[kBC][D + 1], Vs[kBC][D + 1];
   __shared__ float dSs[kBR][kBC + 1];
@@ -197,6 +215,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
   load_rows<D, D + 1>(dOs, dO + head, q0, kBR, N);
   const float lse = q < N ? LSE[bh * N + q] : 0.f;
   const float del = q < N ? Delta[bh * N + q] : 0.f;
+  const float* brow = q < N ? bias_row(bias, bh, q) : nullptr;
   float dq[DS];
 #pragma unroll
   for (int x = 0; x < DS; ++x) dq[x] = 0.f;
@@ -214,8 +233,8 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
         sd = fmaf(Qs[r][x], Ks[c][x], sd);
         dpd = fmaf(dOs[r][x], Vs[c][x], dpd);
       }
-      const bool valid = key < N && q < N && (!CAUSAL || key <= q);
-      const float p = valid ? expf(sd * scale - lse) : 0.f;
+      const bool valid = key < N && q < N && (!CAUSAL || key <= q) && lse != -INFINITY;
+      const float p = valid ? expf(sd * scale + (brow ? brow[key] : 0.f) - lse) : 0.f;
       dSs[r][c] = p * (dpd - del);
     }
     __syncthreads();
@@ -291,7 +310,7 @@ static hipError_t fwd_f32_t(const FwdArgs& a) {
   const long nq = (a.N + kBR - 1) / kBR;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nq)), dim3(256), 0,
                      a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                     (float*)a.o, a.lse, a.N, a.scale);
+                     (float*)a.o, a.lse, a.N, a.scale, a.bias);
   return hipGetLastError();
 }
 
@@ -306,7 +325,7 @@ static hipError_t dkdv_f32_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nb)), dim3(256), 0,
                      a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
                      (const float*)a.dout, a.lse, a.delta, (float*)a.dk, (float*)a.dv, a.N,
-                     a.scale);
+                     a.scale, a.bias);
   return hipGetLastError();
 }
 
@@ -315,7 +334,7 @@ static hipError_t dq_f32_t(const BwdArgs& a) {
   const long nb = (a.N + kBR - 1) / kBR;
   hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nb)), dim3(256), 0,
                      a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                     (const float*)a.dout, a.lse, a.delta, (float*)a.dq, a.N, a.scale);
+                     (const float*)a.dout, a.lse, a.delta, (float*)a.dq, a.N, a.scale, a.bias);
   return hipGetLastError();
 }
 

@@ -28,18 +28,37 @@ fa_status check_sizes(int B, int H, int N, int d, bool* empty) {
   return FA_OK;
 }
 
+// An additive bias: null (none), or 16-byte aligned float32 with strides in
+// elements that are non-negative multiples of 4, and one (b, h) slice --
+// (N - 1) * sq + N elements -- addressable with 32-bit byte offsets (with room
+// for the reads of a ragged last tile, which the kernels mask).
+fa_status check_bias(const float* p, long long sb, long long sh, long long sq, int H, int N,
+                     fa::Bias* b) {
+  *b = fa::Bias{};
+  if (!p) return FA_OK;
+  if (!aligned(p, 16)) return FA_ERR_INVALID_ARG;
+  if (sb < 0 || sh < 0 || sq < 0 || (sb & 3) || (sh & 3) || (sq & 3)) return FA_ERR_INVALID_ARG;
+  const long long nn = N > 0 ? N : 1;
+  if (sq > (1LL << 32) / nn) return FA_ERR_INVALID_ARG;
+  const long long extent = (nn - 1) * sq + nn;
+  if (extent * 4 + 4096 > (1LL << 32)) return FA_ERR_INVALID_ARG;
+  b->p = p;
+  b->sb = sb;
+  b->sh = sh;
+  b->sq = sq;
+  b->H = H > 0 ? H : 1;
+  b->head_bytes = (uint32_t)(extent * 4);
+  return FA_OK;
+}
+
 size_t ws_bytes(long BH, int N) {
   const size_t delta = (size_t)BH * (size_t)N * sizeof(float);
   return (delta + 255) & ~(size_t)255;
 }
 
-}  // namespace
-
-extern "C" {
-
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                 int N, int d, float scale, int causal, int dtype, float q_descale,
-                 float k_descale, float v_descale, void* stream) {
+fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int N, int d, float scale, int causal, int dtype, float q_descale,
+                  float k_descale, float v_descale, const fa::Bias& bias, void* stream) {
   if (dtype != FA_FP32 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   bool empty = false;
@@ -69,6 +88,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   a.q_descale = q_descale;
   a.k_descale = k_descale;
   a.v_descale = v_descale;
+  a.bias = bias;
   a.stream = (hipStream_t)stream;
   hipError_t e;
   switch (dtype) {
@@ -77,6 +97,28 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     default: e = fa::launch_fwd_fp8(a); break;
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, int dtype, float q_descale,
+                 float k_descale, float v_descale, void* stream) {
+  return run_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, q_descale, k_descale,
+                 v_descale, fa::Bias{}, stream);
+}
+
+fa_status fa_fwd_bias(const void* q, const void* k, const void* v, const float* bias,
+                      long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
+                      void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+                      int dtype, void* stream) {
+  if (dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
+  fa::Bias b;
+  const fa_status st = check_bias(bias, bias_stride_b, bias_stride_h, bias_stride_q, H, N, &b);
+  if (st != FA_OK) return st;
+  return run_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, 1.f, 1.f, 1.f, b, stream);
 }
 
 fa_status fa_fwd_mxfp8(const void* q, const void* k, const void* v, const void* q_scale,
@@ -127,7 +169,7 @@ enum { kStageDelta = 1, kStageDkDv = 2, kStageDq = 4 };
 fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
-                  int dtype, void* stream, int stages) {
+                  int dtype, void* stream, int stages, const fa::Bias& bias = fa::Bias{}) {
   if (dtype != FA_FP32 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   bool empty = false;
@@ -160,6 +202,7 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   a.d = d;
   a.scale = scale;
   a.causal = causal != 0;
+  a.bias = bias;
   a.stream = (hipStream_t)stream;
   const bool bf16 = dtype == FA_BF16;
   hipError_t e = hipSuccess;
@@ -188,6 +231,18 @@ fa_status fa_bwd(FA_BWD_PARAMS) {
 fa_status fa_bwd_delta(FA_BWD_PARAMS) { return run_bwd(FA_BWD_ARGS, kStageDelta); }
 fa_status fa_bwd_dkdv(FA_BWD_PARAMS) { return run_bwd(FA_BWD_ARGS, kStageDkDv); }
 fa_status fa_bwd_dq(FA_BWD_PARAMS) { return run_bwd(FA_BWD_ARGS, kStageDq); }
+
+fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const float* bias,
+                      long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
+                      const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                      void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N,
+                      int d, float scale, int causal, int dtype, void* stream) {
+  if (dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
+  fa::Bias b;
+  const fa_status st = check_bias(bias, bias_stride_b, bias_stride_h, bias_stride_q, H, N, &b);
+  if (st != FA_OK) return st;
+  return run_bwd(FA_BWD_ARGS, kStageDelta | kStageDkDv | kStageDq, b);
+}
 
 const char* fa_status_string(int status) {
   switch (status) {

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_kernels.h"
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -67,6 +69,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
                                            (int)(bytes > 0 ? bytes : 0), 0x00020000);
 }
+// Loads into registers through a buffer resource (reads past num_records
+// return zeros): 16 or 4 bytes per lane at voff + soff + imm.
+template <int IMM = 0>
+__device__ __forceinline__ f32x4 buffer_load_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                   uint32_t soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + IMM, soff, 0));
+}
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+// The (b, h) slice of an additive bias as a buffer resource.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bias_rsrc(const Bias& b, uint32_t bh) {
+  const uint32_t bi = bh / (uint32_t)b.H, hi = bh - bi * (uint32_t)b.H;
+  return make_rsrc(b.p + (long long)bi * b.sb + (long long)hi * b.sh, (long)b.head_bytes);
+}
+
 // Direct load of 16 bytes per lane, from byte offset voff of the resource, to
 // LDS at dst + 16 * lane.  The LDS address is wave-uniform (it goes to M0).
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, const void* dst, uint32_t voff) {

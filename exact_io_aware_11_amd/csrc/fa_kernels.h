@@ -8,6 +8,17 @@
 
 namespace fa {
 
+// Additive bias on the scaled scores (float32), s_ij = scale q_i.k_j + b_ij;
+// -inf masks a key.  Element (b, h, i, j) is p[b*sb + h*sh + i*sq + j]; strides
+// are in elements (multiples of 4, or 0 to broadcast), p is 16-byte aligned.
+// head_bytes = ((N - 1) sq + N) * 4, the extent of one (b, h) slice, < 2^32.
+struct Bias {
+  const float* p = nullptr;
+  long long sb = 0, sh = 0, sq = 0;
+  int H = 1;  // heads per batch entry: splits the combined index bh into (b, h)
+  uint32_t head_bytes = 0;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -24,6 +35,7 @@ struct FwdArgs {
   const uint8_t* q_scale = nullptr;
   const uint8_t* k_scale = nullptr;
   const uint8_t* v_scale = nullptr;
+  Bias bias;  // p == nullptr: none
   hipStream_t stream;
 };
 
@@ -42,6 +54,7 @@ struct BwdArgs {
   int N, d;
   float scale;
   bool causal;
+  Bias bias;  // p == nullptr: none
   hipStream_t stream;
 };
 

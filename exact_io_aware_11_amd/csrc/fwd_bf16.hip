@@ -25,6 +25,11 @@
 //  * K and V tiles are double-buffered in LDS (16-byte XOR swizzle), staged
 //    from HBM with 16-byte loads issued one tile ahead; one barrier per tile.
 //  * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA.
+//  * Optional additive bias (the explainer's V2 section merges mask and bias
+//    into the score stage): the next tile's bias values are loaded at the
+//    start of a step, 16 bytes of four consecutive keys per load, and added to
+//    the raw scores (as bias / scale) where the row max is taken; -inf masks.
+//    A row that sees no finite score ends with O = 0 and LSE = -inf.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -32,11 +37,11 @@
 
 namespace fa {
 
-template <int D, bool CAUSAL, int WAVES>
+template <int D, bool CAUSAL, int WAVES, bool BIAS>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int N,
-    uint32_t n_qblk, uint32_t total, float scale, float scale_log2, float grow_thr) {
+    uint32_t n_qblk, uint32_t total, float scale, float scale_log2, float grow_thr, Bias bias) {
   constexpr int BM = 32 * WAVES, BN = 64, TILE = BN * D;  // TILE: elements of one K or V tile
   constexpr int LPW = TILE * 2 / 1024 / WAVES;            // 1 KiB direct loads per wave per tile
   // Two K and two V tile buffers as four separate arrays: the compiler tells
@@ -69,6 +74,24 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
 
   const int q0 = (int)qblk * BM + wave * 32;  // first query row of this wave
   const int qrow = q0 + r32;                  // the query of this lane's column
+
+  // Additive bias: a buffer resource over this (b, h) slice and the byte
+  // offset of this lane's row (rows past N read row N - 1; they are never
+  // written).  Element i of key half b of a tile at key0 is key
+  // key0 + 32 b + 8 (i / 4) + 4 g + i % 4: load x = 4 b + i / 4, component i % 4.
+  [[maybe_unused]] const auto brs = BIAS ? bias_rsrc(bias, bh) : make_rsrc(nullptr, 0);
+  [[maybe_unused]] const uint32_t bvoff =
+      BIAS ? (uint32_t)((long long)min(qrow, N - 1) * bias.sq * 4 + 16 * g) : 0u;
+  [[maybe_unused]] const float inv_scale = 1.f / scale;
+  auto load_bias = [&](f32x4 (&bv)[8], int key0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      bv[x] = buffer_load_f32x4(brs, bvoff + 128 * (x >> 2) + 32 * (x & 3), (uint32_t)key0 * 4u);
+  };
+  auto add_bias = [&](const f32x4 (&bv)[8], f32x16& s0, f32x16& s1, int i) __attribute__((always_inline)) {
+    s0[i] = fmaf(bv[i >> 2][i & 3], inv_scale, s0[i]);
+    s1[i] = fmaf(bv[4 + (i >> 2)][i & 3], inv_scale, s1[i]);
+  };
 
   // Q fragment as the B operand of S^T = K Q^T: lane holds Q[qrow][16t + 8g .. +7].
   bf16x8 qf[D / 16];
@@ -124,6 +147,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
+  // exp2 argument offset for the reference max; 0 while a row has seen no
+  // finite score (all its scores so far are -inf, whose exp is 0).
+  auto neg_ref = [&]() __attribute__((always_inline)) -> float {
+    if constexpr (BIAS) return m_run == -INFINITY ? 0.f : -m_run * scale_log2;
+    else return -m_run * scale_log2;
+  };
 
   auto scores = [&](const uint16_t* Kt, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
     s0 = mfma_bf16(lds_read_b128(Kt + koff[0]), qf[0], f32x16{});
@@ -161,7 +190,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
   // Rescale to a new reference max (rare; see rowmax_guard).
   auto rescale = [&](float mx) __attribute__((always_inline)) {
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2_fast((m_run - m_new) * scale_log2);
+    float alpha = exp2_fast((m_run - m_new) * scale_log2);
+    if constexpr (BIAS) alpha = m_new == -INFINITY ? 1.f : alpha;  // nothing seen yet
     l_run *= alpha;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
@@ -190,7 +220,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
   // P = exp(S - m_run) in place; row sum over the float32 P; P in bf16 out.
   auto exps = [&](f32x16& s0, f32x16& s1, bf16x8& p00, bf16x8& p01, bf16x8& p10,
                   bf16x8& p11) __attribute__((always_inline)) {
-    const float mneg = -m_run * scale_log2;
+    const float mneg = neg_ref();
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -237,6 +267,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
   barrier_vm<0>();
   stage(Kh, lk1, BN);  // (a tile past the end arrives as zeros; never used)
   scores(lk0, sa0, sa1);
+  if constexpr (BIAS) {
+    f32x4 bv0[8];
+    load_bias(bv0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) add_bias(bv0, sa0, sa1, i);
+  }
   if (j_full == 0) apply_mask(sa0, sa1, 0);
   rowmax_guard(sa0, sa1);
 
@@ -264,8 +300,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     const uint16_t* Vt = vtile(parity);
     uint16_t* Vdst = vtile(PN{});
     uint16_t* Kdst = ktile(parity);
-    const float mneg = -m_run * scale_log2;
+    const float mneg = neg_ref();
     const int key1 = (j + 1) * BN;
+    [[maybe_unused]] f32x4 bv[8];  // bias of tile j + 1, loaded before this step's staging
+    if constexpr (BIAS) load_bias(bv, key1);
     const auto kres = tile_rsrc(Kh, (j + 2) * BN);
     const auto vres = tile_rsrc(Vh, (j + 1) * BN);
     bf16x8 pk[4];
@@ -310,9 +348,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
       if (ph == 2 && (e & 7) == 7) pk[e >> 3] = to_bf16x8(sv, i - 7);
     };
     auto mask_next = [&](int i) __attribute__((always_inline)) {  // element i of both halves of S_{j+1}
-      const int key = key1 + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (key >= N || (CAUSAL && key > qrow)) sn0[i] = -INFINITY;
-      if (key + 32 >= N || (CAUSAL && key + 32 > qrow)) sn1[i] = -INFINITY;
+      if constexpr (BIAS) add_bias(bv, sn0, sn1, i);
+      if constexpr (MASK_NEXT) {
+        const int key = key1 + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key >= N || (CAUSAL && key > qrow)) sn0[i] = -INFINITY;
+        if (key + 32 >= N || (CAUSAL && key + 32 > qrow)) sn1[i] = -INFINITY;
+      }
     };
     // Elements start phase (a) over products 0 .. EXP_OPS-1; phase (c) of the
     // last element of key chunk kc lands two products later, before product
@@ -332,7 +373,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
         const int r = k - (NOPS - 12);
 #pragma unroll
         for (int i = r * 16 / 12; i < (r + 1) * 16 / 12; ++i) {
-          if constexpr (MASK_NEXT) mask_next(i);
+          if constexpr (MASK_NEXT || BIAS) mask_next(i);
           mxp[i & 1] = fmaxf(mxp[i & 1], fmaxf(sn0[i], sn1[i]));
           pin(mxp[i & 1]);
         }
@@ -387,7 +428,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
   wait_vm<0>();  // no direct load may still be landing when the workgroup ends
 
   const float l_tot = halves_sum(l_run);
-  const float inv = 1.f / l_tot;
+  // (with a bias, a row that saw no finite score has l = 0: O = 0, LSE = -inf)
+  const bool empty_row = BIAS && l_tot == 0.f;
+  const float inv = empty_row ? 0.f : 1.f / l_tot;
   if (qrow < N) {
     uint16_t* Orow = O + head + (size_t)qrow * D;
 #pragma unroll
@@ -399,29 +442,35 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
         for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[cb][4 * q4 + e] * inv);
         *reinterpret_cast<bf16x4*>(Orow + 32 * cb + 8 * q4 + 4 * g) = v;
       }
-    if (g == 0) LSE[(size_t)bh * N + qrow] = m_run * scale + __logf(l_tot);
+    if (g == 0) LSE[(size_t)bh * N + qrow] = empty_row ? -INFINITY : m_run * scale + __logf(l_tot);
   }
-}
-
-template <int D, bool CAUSAL, int WAVES>
-static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
-  constexpr int BM = 32 * WAVES;
-  const uint32_t n_qblk = (uint32_t)((a.N + BM - 1) / BM);
-  const uint32_t total = (uint32_t)(a.BH * n_qblk);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WAVES>), dim3(total), dim3(64 * WAVES), 0,
-                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.N, n_qblk, total, a.scale, a.scale * kLog2e,
-                     kRescaleLog2 / (a.scale * kLog2e));
-  return hipGetLastError();
 }
 
 #ifndef FA_FWD_WAVES
 #define FA_FWD_WAVES 4
 #endif
-hipError_t launch_fwd_bf16(const FwdArgs& a) {
+template <int D, bool CAUSAL, int WAVES, bool BIAS>
+static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
+  constexpr int BM = 32 * WAVES;
+  const uint32_t n_qblk = (uint32_t)((a.N + BM - 1) / BM);
+  const uint32_t total = (uint32_t)(a.BH * n_qblk);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WAVES, BIAS>), dim3(total), dim3(64 * WAVES), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.o, a.lse, a.N, n_qblk, total, a.scale, a.scale * kLog2e,
+                     kRescaleLog2 / (a.scale * kLog2e), a.bias);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_bf16_b(const FwdArgs& a) {
   constexpr int W = FA_FWD_WAVES;
-  if (a.d == 64) return a.causal ? launch_fwd_bf16_t<64, true, W>(a) : launch_fwd_bf16_t<64, false, W>(a);
-  return a.causal ? launch_fwd_bf16_t<128, true, W>(a) : launch_fwd_bf16_t<128, false, W>(a);
+  return a.bias.p ? launch_fwd_bf16_t<D, CAUSAL, W, true>(a)
+                  : launch_fwd_bf16_t<D, CAUSAL, W, false>(a);
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_fwd_bf16_b<64, true>(a) : launch_fwd_bf16_b<64, false>(a);
+  return a.causal ? launch_fwd_bf16_b<128, true>(a) : launch_fwd_bf16_b<128, false>(a);
 }
 
 }  // namespace fa

@@ -19,6 +19,9 @@ Storage formats:
   codes = round-to-nearest-even(X / s) saturated to +-448.  The explainer says
   only that FP8 inputs are paired with scaling factors (V3 section); the
   per-tensor amax form is the plainest reading.
+
+Additive biases (:func:`draw_bias`): float32 arrays in a row-pitched layout,
+values N(0, 1) from their own seed, with -inf entries where a mask is wanted.
 """
 from __future__ import annotations
 
@@ -200,3 +203,45 @@ def make_inputs(shape, dtype: str, seed: int = 42, with_dout: bool = True) -> In
         (cq, sq), (ck, sk), (cv, sv) = (quantize_e4m3fn(t) for t in (q, k, v))
         return Inputs(cq, ck, cv, None, (sq, sk, sv), dtype)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def pitch(n: int) -> int:
+    """A row pitch for an n-key bias row: n rounded up to a multiple of 4 (the
+    strides the library takes), plus 4 so that the pitch always differs from n."""
+    return (n + 3) // 4 * 4 + 4
+
+
+def draw_bias(lead, N: int, seed: int, kind: str = "dense", p_mask: float = 0.1,
+              window: int = 0) -> np.ndarray:
+    """A float32 additive bias for N queries and N keys, in a row-pitched
+    array whose last axis has pitch(N) entries (entries past N are NaN: never
+    read).  `lead` is the leading shape, e.g. (B, H), (1, H) or (1, 1).
+
+    kind:
+      "dense"   -- N(0, 1) values, each entry -inf with probability p_mask
+      "keypad"  -- shape lead + (1, pitch): 0 for keys below a length drawn per
+                   leading index in [1, N], -inf past it (key padding)
+      "window"  -- N(0, 1) values, -inf where key < query - window (a sliding
+                   window; with a causal mask the attention becomes banded)
+    """
+    rng = np.random.default_rng(seed)
+    P = pitch(N)
+    if kind == "keypad":
+        lengths = rng.integers(1, N + 1, size=tuple(lead))
+        b = np.full(tuple(lead) + (1, P), np.nan, np.float32)
+        keys = np.arange(N)
+        b[..., 0, :N] = np.where(keys < lengths[..., None], 0.0, -np.inf)
+        return b
+    b = np.full(tuple(lead) + (N, P), np.nan, np.float32)
+    vals = rng.standard_normal(tuple(lead) + (N, N)).astype(np.float32)
+    if kind == "dense":
+        vals[rng.random(vals.shape) < p_mask] = -np.inf
+    elif kind == "window":
+        i = np.arange(N)[:, None]
+        j = np.arange(N)[None, :]
+        vals[..., j < i - window] = -np.inf
+    else:
+        raise ValueError(kind)
+    b[..., :N] = vals
+    return b
+

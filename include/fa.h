@@ -93,6 +93,30 @@ fa_status fa_fwd_mxfp8(const void* q, const void* k, const void* v, const void* 
                        const void* k_scale, const void* v_scale, void* o, float* lse, int B,
                        int H, int N, int d, float scale, int causal, void* stream);
 
+/* Forward pass with an additive bias on the scaled scores: the explainer's
+ * V2 section merges mask and bias into the score computation.
+ *   s_ij = scale * q_i . k_j + bias[b][h][i][j]
+ * then the softmax over the visible keys (all, or j <= i with causal = 1).
+ * A bias of -INFINITY masks a key, so general masks are biases of 0 and -inf
+ * (key padding, sliding windows, block patterns ...).  Bias values must be
+ * finite or -inf.  A row whose visible scores are all -inf has an empty
+ * softmax: its output row is 0 and its LSE is -inf.
+ *   bias   : float32, element (b, h, i, j) at
+ *            bias[b*bias_stride_b + h*bias_stride_h + i*bias_stride_q + j];
+ *            strides in elements, each a non-negative multiple of 4 (0
+ *            broadcasts: a [1,1,N,N] bias has strides 0, 0, row pitch; a
+ *            per-key [B,1,1,N] padding mask has strides pitch, 0, 0).  The
+ *            pointer is 16-byte aligned and the caller owns the buffer.  One
+ *            (b, h) slice, (N-1)*bias_stride_q + N elements, must stay below
+ *            2^30 - 1024 elements.  NULL means no bias (exactly fa_fwd).
+ * dtype: FA_FP32 or FA_BF16 (FA_FP8_E4M3 returns FA_ERR_UNSUPPORTED).  The
+ * other arguments are those of fa_fwd.  Same status codes; nothing is
+ * launched on an error. */
+fa_status fa_fwd_bias(const void* q, const void* k, const void* v, const float* bias,
+                      long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
+                      void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+                      int dtype, void* stream);
+
 /* Bytes of device workspace fa_bwd needs for these sizes (delta, one float32
  * per row, at the start of the workspace).  Returns 0 for invalid sizes. */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
@@ -134,6 +158,18 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, 
                     const float* lse, void* dq, void* dk, void* dv, void* workspace,
                     size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
                     int dtype, void* stream);
+
+/* Backward pass with the additive bias of fa_fwd_bias: P is recomputed as
+ * exp(scale q.k + bias - LSE) from the LSE that fa_fwd_bias wrote (rows with
+ * LSE = -inf have P = 0 and add nothing).  The bias is an input: no gradient
+ * is formed for it.  Arguments as fa_bwd plus the bias of fa_fwd_bias;
+ * enqueues the delta, dK/dV and dQ kernels.  FA_FP8_E4M3 returns
+ * FA_ERR_UNSUPPORTED. */
+fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const float* bias,
+                      long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
+                      const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                      void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N,
+                      int d, float scale, int causal, int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -25,9 +25,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
-                                    "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_mxfp8",
-                                    "fa_status_string"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_bias", "fa_bwd_delta", "fa_bwd_dkdv",
+                                    "fa_bwd_dq", "fa_bwd_workspace_size", "fa_fwd",
+                                    "fa_fwd_bias", "fa_fwd_mxfp8", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -65,6 +65,41 @@ def test_fwd_mxfp8_rejects_before_launch(kw, status):
 
 def test_fwd_mxfp8_empty_is_a_noop():
     assert fwd_mx(N=0, qs=0, ks=0, vs=0) == OK and fwd_mx(B=0) == OK
+
+
+def fwd_b(**kw):
+    a = dict(q=P, k=P, v=P, bias=P, sb=0, sh=0, sq=16, o=P, lse=P, B=1, H=1, N=16, d=64,
+             scale=0.125, causal=0, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return lib.fa_fwd_bias(a["q"], a["k"], a["v"], a["bias"], a["sb"], a["sh"], a["sq"], a["o"],
+                           a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                           a["dtype"], a["stream"])
+
+
+def bwd_b(**kw):
+    a = dict(q=P, k=P, v=P, bias=P, sb=0, sh=0, sq=16, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P,
+             wsb=1 << 20, B=1, H=1, N=16, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16,
+             stream=None)
+    a.update(kw)
+    return lib.fa_bwd_bias(a["q"], a["k"], a["v"], a["bias"], a["sb"], a["sh"], a["sq"], a["o"],
+                           a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], a["B"],
+                           a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+                           a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_FP8_E4M3), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+    (dict(bias=P + 4), INVALID), (dict(sq=18), INVALID), (dict(sb=-4), INVALID),
+    (dict(sh=2), INVALID), (dict(sq=1 << 30), INVALID), (dict(N=1 << 16, sq=1 << 16), INVALID),
+    (dict(q=0), INVALID), (dict(scale=0.0), INVALID), (dict(causal=2), INVALID),
+])
+@pytest.mark.parametrize("fn", [fwd_b, bwd_b])
+def test_bias_entry_points_reject_before_launch(kw, status, fn):
+    assert fn(**kw) == status
+
+
+def test_bias_entry_points_empty_is_a_noop():
+    assert fwd_b(N=0) == OK and fwd_b(B=0, bias=0) == OK and bwd_b(H=0) == OK
 
 
 def bwd(fn="fa_bwd", **kw):
