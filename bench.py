@@ -10,8 +10,11 @@ HIP events on the stream it runs on, so per-kernel durations are measured live.
 
 After the timed steps the forward-only workloads (bf16 causal N=8192 d=128,
 bf16 N=2048 d=64, fp8 N=16384 d=128 with per-tensor scales and with e8m0
-block scales) are timed the same way and reported in the same JSON line, and the CPU oracle is timed on a bounded sample of the
-main workload on this host's cores.
+block scales) and two runs with an additive bias on the scores (the N=8192
+forward with a dense bias, the default workload's forward and backward with a
+sliding-window bias) are timed the same way and reported in the same JSON
+line, and the CPU oracle is timed on a bounded sample of the main workload on
+this host's cores.
 
 Prints ONE JSON line.  Only N=1 GPU is supported (--gpus > 1 exits).
 """
@@ -34,6 +37,13 @@ METRIC = "attention fwd/bwd TFLOPS (bf16, fp8) and % of MI355X MFMA peak"
 MAIN = "bf16_causal_fwdbwd_b2h16n4096d128"
 EXTRA = ["bf16_causal_fwd_b2h32n8192d128", "bf16_fwd_b4h16n2048d64", "fp8_fwd_b1h32n16384d128"]
 MX_EXTRA = ("mxfp8_fwd_b1h32n16384d128", (1, 32, 16384, 128))
+# Additive bias on the scores (one [N, N] float32 bias shared by every batch
+# entry and head): (name, shape, causal, bias kind, window, with backward)
+BIAS_EXTRA = [
+    ("bf16_causal_fwd_densebias_b2h32n8192d128", (2, 32, 8192, 128), True, "dense", 0, False),
+    ("bf16_causal_fwdbwd_windowbias_b2h16n4096d128", (2, 16, 4096, 128), True, "window", 1023,
+     True),
+]
 
 
 # The sources each timed kernel is built from (with the build flags): a
@@ -243,6 +253,49 @@ def time_fwd_mx(shape, reps, warmup, warm_s=0.0):
     return res
 
 
+def time_bias(shape, causal, kind, window, backward, reps, warmup, warm_s=0.0):
+    """fa_fwd_bias (and fa_bwd_bias) with a shared [N, N] bias drawn by
+    fa_inputs.draw_bias (N(0,1); "dense": 10 % -inf, "window": -inf before the
+    last window+1 keys).  The kernels apply the bias element by element, so the
+    algorithmic FLOPs are those of the unbiased problem."""
+    import torch
+
+    import exact_io_aware_11_amd as fa
+    import fa_inputs
+
+    B, H, N, d = shape
+    inp = fa_inputs.make_inputs(shape, "bf16", seed=42, with_dout=backward)
+
+    def dev(a):
+        return torch.from_numpy(a).view(torch.int16).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    bias = torch.from_numpy(fa_inputs.draw_bias((1, 1), N, seed=7, kind=kind,
+                                                window=window)).cuda()[..., :N]
+    o = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    out = {}
+    mean, med = time_calls(lambda: fa.fa_fwd_bias(q, k, v, bias, o, lse, scale, causal),
+                           reps, warmup, warm_s)
+    out["fwd"] = {"ms": round(mean, 4), "ms_median": round(med, 4),
+                  "TFLOP/s": round(fa.flops_fwd(B, H, N, d, causal) / (mean * 1e-3) / 1e12, 1)}
+    if backward:
+        do = dev(inp.dout)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device="cuda")
+        mean, med = time_calls(
+            lambda: fa.fa_bwd_bias(q, k, v, bias, o, do, lse, dq, dk, dv, ws, scale, causal),
+            reps, warmup, warm_s)
+        out["bwd"] = {"ms": round(mean, 4), "ms_median": round(med, 4),
+                      "TFLOP/s": round(fa.flops_bwd(B, H, N, d, causal) / (mean * 1e-3) / 1e12,
+                                       1)}
+        del do, dq, dk, dv, ws
+    del q, k, v, bias, o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, max_heads):
     """The oracle as it stands on a bounded sample: whole heads of the workload."""
     import numpy as np
@@ -357,6 +410,7 @@ def main():
     log(f"step {ms:.3f} ms  {value:.1f} TFLOP/s  kernels {kernels}")
 
     extra = {}
+    bias_lines = {}
     if not args.no_extra:
         for name in EXTRA:
             if name == w.name:
@@ -378,6 +432,11 @@ def main():
                        "frac_of_peak": round(tf / PEAK_TFLOPS["fp8"], 4),
                        "peak": PEAK_TFLOPS["fp8"]}
         log(f"{name}: {mean:.3f} ms {tf:.1f} TFLOP/s")
+        for name, shape, causal, kind, window, backward in BIAS_EXTRA:
+            r = time_bias(shape, causal, kind, window, backward, reps=max(10, args.steps // 2),
+                          warmup=3, warm_s=min(args.warm_seconds, 1.0))
+            bias_lines[name] = r
+            log(f"{name}: {r}")
 
     cpu = None
     if not args.no_cpu:
@@ -399,6 +458,7 @@ def main():
         "kernels": kernels,
         "roofline": roof,
         "forward_workloads": extra,
+        "bias_workloads": bias_lines,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
     }

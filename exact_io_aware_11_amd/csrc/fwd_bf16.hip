@@ -26,10 +26,11 @@
 //    from HBM with 16-byte loads issued one tile ahead; one barrier per tile.
 //  * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA.
 //  * Optional additive bias (the explainer's V2 section merges mask and bias
-//    into the score stage): the next tile's bias values are loaded at the
-//    start of a step, 16 bytes of four consecutive keys per load, and added to
-//    the raw scores (as bias / scale) where the row max is taken; -inf masks.
-//    A row that sees no finite score ends with O = 0 and LSE = -inf.
+//    into the score stage): a tile's bias values are loaded one step before
+//    the step that uses them (16 bytes of four consecutive keys per load, two
+//    register buffers), so the per-step barrier's wait covers them, and added
+//    to the raw scores (as bias / scale) where the row max is taken; -inf
+//    masks.  A row that sees no finite score ends with O = 0 and LSE = -inf.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -37,8 +38,10 @@
 
 namespace fa {
 
+// (With a bias, one workgroup per CU: the bias of the tile after next is held
+// in registers for a whole step, which needs more than half the register file.)
 template <int D, bool CAUSAL, int WAVES, bool BIAS>
-__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : 8 / WAVES) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int N,
     uint32_t n_qblk, uint32_t total, float scale, float scale_log2, float grow_thr, Bias bias) {
@@ -266,12 +269,17 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
   stage(Vh, lv0, 0);
   barrier_vm<0>();
   stage(Kh, lk1, BN);  // (a tile past the end arrives as zeros; never used)
-  scores(lk0, sa0, sa1);
+  // bias of tile t lives in bvb[t % 2] from the step before it is used
+  [[maybe_unused]] f32x4 bvb[2][8];
   if constexpr (BIAS) {
     f32x4 bv0[8];
     load_bias(bv0, 0);
+    load_bias(bvb[1], BN);
+    scores(lk0, sa0, sa1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) add_bias(bv0, sa0, sa1, i);
+  } else {
+    scores(lk0, sa0, sa1);
   }
   if (j_full == 0) apply_mask(sa0, sa1, 0);
   rowmax_guard(sa0, sa1);
@@ -302,8 +310,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     uint16_t* Kdst = ktile(parity);
     const float mneg = neg_ref();
     const int key1 = (j + 1) * BN;
-    [[maybe_unused]] f32x4 bv[8];  // bias of tile j + 1, loaded before this step's staging
-    if constexpr (BIAS) load_bias(bv, key1);
+    // bias: tile j + 1's (used below) arrived during step j - 1; tile j + 2's
+    // goes into the buffer tile j's used, ahead of this step's staging loads
+    [[maybe_unused]] f32x4(&bv)[8] = bvb[P ^ 1];
+    if constexpr (BIAS) load_bias(bvb[P], key1 + BN);
     const auto kres = tile_rsrc(Kh, (j + 2) * BN);
     const auto vres = tile_rsrc(Vh, (j + 1) * BN);
     bf16x8 pk[4];
