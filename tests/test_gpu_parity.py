@@ -224,3 +224,40 @@ def test_bad_arguments_raise_without_launch():
     with pytest.raises(fa.FAError) as e:
         fa.fa_bwd(y, y, y, y, y, l8, y, y, y, ws, 0.1, False)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
+
+
+# --------------------------------------------------------------------------- #
+# Launch-order branches and the largest sequence the tests run
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 8, 1024, 64, True),    # 8 blocks per head, 64 blocks: one head per XCD range
+    (2, 8, 512, 128, True),    # 4 blocks per head: two heads per XCD range
+    (1, 3, 1024, 64, True),    # 24 blocks: XCD remap without whole heads per range
+    (1, 5, 384, 128, False),   # 15 blocks: plain order
+])
+def test_bf16_block_orders(B, H, N, d, causal):
+    """Every kernel maps workgroup ids to (head, block) differently depending on
+    how the grid divides over the 8 XCDs; each branch must still cover every
+    block exactly once (a missed block leaves NaN, a doubled one is harmless
+    but a wrong map shows as a mismatch)."""
+    inp = fa_inputs.make_inputs((B, H, N, d), "bf16", seed=B * 100 + H * 10 + N)
+    full_check_bwd(inp, 1 / math.sqrt(d), causal, f"bf16 order {B}x{H}x{N}x{d}")
+
+
+@pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, False), ("bf16", 128, True),
+                                             ("bf16", 64, True), ("fp8", 128, False)])
+def test_longest_sequence_forward(dtype, d, causal):
+    """N = 2^17 keys in one head: every byte offset the kernels form stays in
+    range (sampled rows, including the last ones, against the oracle)."""
+    N = 1 << 17
+    inp = fa_inputs.make_inputs((1, 1, N, d), dtype, seed=17, with_dout=False)
+    _, o, lse = run_fwd(inp, 1 / math.sqrt(d), causal)
+    o_all, lse_all = to_f64(o), to_f64(lse)
+    assert np.isfinite(o_all).all() and np.isfinite(lse_all).all()
+    rows = np.unique(np.concatenate([sample_rows(N, n=12), [N - 64, N - 63, N // 3]]))
+    qs, ks, vs = (exact_values(x[0, 0], dtype, s)
+                  for x, s in zip((inp.q, inp.k, inp.v), inp.descale))
+    o_ref, lse_ref = oracle.attn_fwd_rows(qs, ks, vs, rows, 1 / math.sqrt(d), causal)
+    check(f"{dtype} N=2^17 d={d} causal={causal} O rows", o_all[0, 0, rows], o_ref, dtype)
+    check(f"{dtype} N=2^17 d={d} causal={causal} LSE rows", lse_all[0, 0, rows], lse_ref, dtype,
+          lse=True)
