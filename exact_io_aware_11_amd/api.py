@@ -33,7 +33,15 @@ def _shape(q):
     return tuple(int(x) for x in q.shape)
 
 
+def _check_device(name, t):
+    """The kernels dereference the pointers on the GPU: host tensors must not
+    reach them."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
 def _check_like(name, t, shape):
+    _check_device(name, t)
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
@@ -106,6 +114,7 @@ def _bias_view(bias, B, H, N):
     """A float32 bias tensor broadcast to [B, H, N, N]: (pointer, strides b, h, q)."""
     import torch
 
+    _check_device("bias", bias)
     if bias.dtype != torch.float32:
         raise TypeError("bias must be float32")
     if bias.dim() != 4:
@@ -157,6 +166,7 @@ def fa_bwd_bias(q, k, v, bias, o, dout, lse, dq, dk, dv, workspace, scale: float
     _check_dtypes(code, (("k", k), ("v", v), ("o", o), ("dout", dout)),
                   (("dq", dq), ("dk", dk), ("dv", dv)))
     bp, sb, sh, sq = _bias_view(bias, B, H, N)
+    _check_device("workspace", workspace)
     nbytes = workspace.numel() * workspace.element_size()
     st = lib.fa_bwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), bp, sb, sh, sq, o.data_ptr(),
                          dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
@@ -181,6 +191,7 @@ def _bwd_call(fn_name, q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, caus
         raise FAError(2, f"{fn_name}: the backward takes float32 or bfloat16 tensors")
     _check_dtypes(code, (("k", k), ("v", v), ("o", o), ("dout", dout)),
                   (("dq", dq), ("dk", dk), ("dv", dv)))
+    _check_device("workspace", workspace)
     nbytes = workspace.numel() * workspace.element_size()
     st = getattr(lib, fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),

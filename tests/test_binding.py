@@ -1,0 +1,30 @@
+"""The Python binding refuses what the C ABI cannot check: host tensors,
+wrong shapes and mixed element types never reach a kernel.  (No GPU needed:
+every call here raises before the library is called.)"""
+import pytest
+
+torch = pytest.importorskip("torch")
+fa = pytest.importorskip("exact_io_aware_11_amd")
+
+
+def host(shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_host_tensors_are_rejected():
+    x, lse = host((1, 1, 8, 64)), host((1, 1, 8), torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.fa_fwd(x, x, x, x, lse, 0.125, False)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.fa_fwd_bias(x, x, x, host((1, 1, 8, 8), torch.float32), x, lse, 0.125, False)
+    ws = host((256,), torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.fa_bwd(x, x, x, x, x, lse, x, x, x, ws, 0.125, False)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.fa_bwd_bias(x, x, x, host((1, 1, 8, 8), torch.float32), x, x, lse, x, x, x, ws, 0.125,
+                       False)
+    codes, sc = host((1, 1, 8, 64), torch.uint8), host((1, 1, 8, 4), torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.fa_fwd_mxfp8(codes, codes, codes, sc, sc, host((1, 1, 1, 64), torch.uint8), x, lse,
+                        0.125, False)
+
