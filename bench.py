@@ -13,8 +13,9 @@ bf16 N=2048 d=64, fp8 N=16384 d=128 with per-tensor scales and with e8m0
 block scales) and two runs with an additive bias on the scores (the N=8192
 forward with a dense bias, the default workload's forward and backward with a
 sliding-window bias) are timed the same way and reported in the same JSON
-line, and the CPU oracle is timed on a bounded sample of the main workload on
-this host's cores.
+line, as is the launch-bound float32 workload (N=128, in microseconds), and
+the CPU oracle is timed on a bounded sample of the main workload on this
+host's cores.
 
 Prints ONE JSON line.  Only N=1 GPU is supported (--gpus > 1 exits).
 """
@@ -231,6 +232,28 @@ def time_fwd_only(w, reps, warmup, warm_s=0.0):
     return res
 
 
+def time_small_fp32(reps=50):
+    """The float32 workload (one head, N=128, d=64, fwd+bwd): four 32-row
+    workgroups per kernel, so launch latency dominates; reported in microseconds."""
+    import torch
+
+    import exact_io_aware_11_amd as fa
+
+    w = __import__("fa_inputs").WORKLOADS["fp32_fwdbwd_b1h1n128d64"]
+    inp, q, k, v, do = device_inputs(w, True)
+    B, H, N, d = w.shape
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device="cuda")
+    f_mean, f_med = time_calls(lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal), reps, 5)
+    b_mean, b_med = time_calls(
+        lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, w.scale, w.causal), reps, 5)
+    return {"fwd_us": round(f_mean * 1e3, 2), "fwd_us_median": round(f_med * 1e3, 2),
+            "bwd_us": round(b_mean * 1e3, 2), "bwd_us_median": round(b_med * 1e3, 2),
+            "note": "event-timed on the stream; launch-bound (4 workgroups per kernel)"}
+
+
 def time_fwd_mx(shape, reps, warmup, warm_s=0.0):
     """The microscaled fp8 forward (one e8m0 scale per 32 elements along each
     product's contraction) on the same shape as the per-tensor fp8 line."""
@@ -362,7 +385,8 @@ def main():
     ap.add_argument("--workload", default=MAIN)
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads the CPU oracle runs (0: all B*H heads of the workload)")
     ap.add_argument("--hbm-calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -432,6 +456,9 @@ def main():
                        "frac_of_peak": round(tf / PEAK_TFLOPS["fp8"], 4),
                        "peak": PEAK_TFLOPS["fp8"]}
         log(f"{name}: {mean:.3f} ms {tf:.1f} TFLOP/s")
+        small = time_small_fp32()
+        extra["fp32_fwdbwd_b1h1n128d64"] = small
+        log(f"fp32_fwdbwd_b1h1n128d64: {small}")
         for name, shape, causal, kind, window, backward in BIAS_EXTRA:
             r = time_bias(shape, causal, kind, window, backward, reps=max(10, args.steps // 2),
                           warmup=3, warm_s=min(args.warm_seconds, 1.0))
@@ -441,7 +468,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")
-        cpu = cpu_baseline(w, args.cpu_heads)
+        cpu = cpu_baseline(w, args.cpu_heads or w.B * w.H)
         log(f"cpu oracle: {cpu}")
 
     out = {
