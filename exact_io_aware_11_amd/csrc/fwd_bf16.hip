@@ -68,13 +68,18 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : 8 / WAVES) void fwd_
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
-  uint32_t bh, qblk;
-  map_block(blockIdx.x, n_qblk, total, CAUSAL ? kOrderHeavyLast : kOrderPlain, bh, qblk);
+  // Causal: a workgroup takes row blocks u and n_qblk - 1 - u, which together
+  // visit the same number of key tiles for every u, so all workgroups carry
+  // equal work and each pays its set-up once per two blocks.
+  const uint32_t n_units = CAUSAL ? (n_qblk + 1) / 2 : n_qblk;
+  uint32_t bh, unit;
+  map_block(blockIdx.x, n_units, total, kOrderPlain, bh, unit);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* Qh = Q + head;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
 
+  auto body = [&](const uint32_t qblk) __attribute__((always_inline)) {
   const int q0 = (int)qblk * BM + wave * 32;  // first query row of this wave
   const int qrow = q0 + r32;                  // the query of this lane's column
 
@@ -454,6 +459,18 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : 8 / WAVES) void fwd_
       }
     if (g == 0) LSE[(size_t)bh * N + qrow] = empty_row ? -INFINITY : m_run * scale + __logf(l_tot);
   }
+  };  // body
+
+  if constexpr (CAUSAL) {
+    const uint32_t partner = n_qblk - 1 - unit;
+    body(partner);  // the longer block first
+    if (partner != unit) {  // uniform over the workgroup
+      barrier_vm<0>();  // every wave is done with the first block's LDS tiles
+      body(unit);
+    }
+  } else {
+    body(unit);
+  }
 }
 
 #ifndef FA_FWD_WAVES
@@ -463,7 +480,8 @@ template <int D, bool CAUSAL, int WAVES, bool BIAS>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   constexpr int BM = 32 * WAVES;
   const uint32_t n_qblk = (uint32_t)((a.N + BM - 1) / BM);
-  const uint32_t total = (uint32_t)(a.BH * n_qblk);
+  const uint32_t n_units = CAUSAL ? (n_qblk + 1) / 2 : n_qblk;  // row blocks paired when causal
+  const uint32_t total = (uint32_t)(a.BH * n_units);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WAVES, BIAS>), dim3(total), dim3(64 * WAVES), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, n_qblk, total, a.scale, a.scale * kLog2e,
