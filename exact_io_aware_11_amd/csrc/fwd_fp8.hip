@@ -60,9 +60,12 @@ __device__ __forceinline__ int tile_byte(int row, int chunk) {
   return row * D + 16 * (chunk ^ sw8<D>(row));
 }
 
+// Four floats to four e4m3fn bytes.  Each conversion writes one 16-bit half of
+// its destination and keeps the other; the first one is seeded with d's own
+// bits (overwritten half by half), so no zero needs to be materialised.
 __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, __float_as_int(d), true);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, false);
   return (uint32_t)w;
 }
 __device__ __forceinline__ i32x4 lds_read_i32x4(const uint8_t* p) {
@@ -386,8 +389,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
         for (int i = r * 16 / NCB; i < (r + 1) * 16 / NCB; ++i) {
           if constexpr (MASK_NEXT) mask_next(i);
           mxp[i & 1] = fmaxf(mxp[i & 1], fmaxf(sn0[i], sn1[i]));
+          asm volatile("" : "+v"(mxp[i & 1]));  // one three-input max per element pair
         }
-        asm volatile("" : "+v"(mxp[0]), "+v"(mxp[1]));
       }
       if (k < 2 * LPW) {  // loads: K_{j+2} pieces, then V_{j+1}
         const int x = k % LPW;
