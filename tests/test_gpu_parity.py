@@ -261,3 +261,26 @@ def test_longest_sequence_forward(dtype, d, causal):
     check(f"{dtype} N=2^17 d={d} causal={causal} O rows", o_all[0, 0, rows], o_ref, dtype)
     check(f"{dtype} N=2^17 d={d} causal={causal} LSE rows", lse_all[0, 0, rows], lse_ref, dtype,
           lse=True)
+
+
+def test_many_heads_fwd_bwd():
+    """B*H = 65536 heads of N = 65 (two row blocks, a ragged one): the largest
+    grids the tests launch (131072 workgroups per forward); sampled heads,
+    including the first and the last, against the oracle."""
+    B, H, N, d = 256, 256, 65, 64
+    inp = fa_inputs.make_inputs((B, H, N, d), "bf16", seed=3)
+    scale = 1 / math.sqrt(d)
+    dev, o, lse = run_fwd(inp, scale, True)
+    (dq, dk, dv), _ = run_bwd(dev, o, lse, inp, scale, True)
+    for (b, h) in [(0, 0), (B - 1, H - 1), (B // 2, 17), (3, H - 1)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        qs, ks, vs, dos = (exact_values(x[sl], "bf16") for x in (inp.q, inp.k, inp.v, inp.dout))
+        o_ref, lse_ref = oracle.attn_fwd(qs, ks, vs, scale, True)
+        tag = f"bf16 256x256x65x64 head ({b},{h})"
+        check(f"{tag} O", to_f64(o[sl]), o_ref, "bf16")
+        check(f"{tag} LSE", to_f64(lse[sl]), lse_ref, "bf16", lse=True)
+        refs = oracle.attn_bwd(qs, ks, vs, dos, scale, True)
+        for name, got, ref in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
+            check(f"{tag} {name}", to_f64(got[sl]), ref, "bf16")
+    for name, t in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert torch.isfinite(t.float()).all(), name
