@@ -7,9 +7,11 @@
 // accumulator rescaled by alpha = exp(m_old - m_new), and one division at the
 // end.  Scores and probabilities live only in registers.
 //
-// Work split (explainer V2 section; FA1 page section 10.2.5): one workgroup
-// of 4 waves per (batch, head, block of 128 query rows); each wave owns 32
-// query rows and scans every visible key tile of 64 keys.
+// Work split (explainer V2 section; FA1 page section 10.2.5): a workgroup of
+// 4 waves handles a (batch, head, block of 128 query rows) -- under the causal
+// mask two blocks, u and n-1-u, one after the other, so that every workgroup
+// visits the same number of key tiles; each wave owns 32 query rows and scans
+// every visible key tile of 64 keys.
 //
 // gfx950 mapping:
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K (A operand) comes from LDS,
