@@ -232,6 +232,27 @@ def time_fwd_only(w, reps, warmup, warm_s=0.0):
     return res
 
 
+def measure_mfma_rates(warm_s=0.5, reps=10):
+    """The matrix-core rate on realistic operand bits (fa_measure_mfma_rate:
+    pure 32x32 products on pseudo-random per-lane data, two waves per SIMD on
+    every CU), after warm-up: the measured ceiling beside the published peak."""
+    import torch
+
+    import exact_io_aware_11_amd as fa
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 8 * cus, 2048
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    rates = {}
+    for name, fp8 in (("bf16", False), ("fp8", True)):
+        flops = fa.fa_measure_mfma_rate(out, blocks, iters, fp8)
+        mean, _ = time_calls(lambda: fa.fa_measure_mfma_rate(out, blocks, iters, fp8), reps, 2,
+                             warm_s)
+        rates[name] = round(flops / (mean * 1e-3) / 1e12, 1)
+    del out
+    return rates
+
+
 def time_small_fp32(reps=50):
     """The float32 workload (one head, N=128, d=64, fwd+bwd): four 32-row
     workgroups per kernel, so launch latency dominates; reported in microseconds."""
@@ -465,6 +486,18 @@ def main():
             bias_lines[name] = r
             log(f"{name}: {r}")
 
+    measured = None
+    if not args.no_extra:
+        measured = measure_mfma_rates()
+        log(f"measured matrix-core rates (TFLOP/s): {measured}")
+        roof["measured_peak"] = measured[w.dtype] if w.dtype in measured else None
+        if roof["unit"] == "TFLOP/s" and roof["measured_peak"]:
+            roof["frac_of_measured_peak"] = round(roof["achieved"] / roof["measured_peak"], 4)
+        for name, x in extra.items():
+            dt = "fp8" if name.startswith(("fp8", "mxfp8")) else "bf16"
+            if "TFLOP/s" in x and dt in measured:
+                x["frac_of_measured_peak"] = round(x["TFLOP/s"] / measured[dt], 4)
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")
@@ -486,6 +519,10 @@ def main():
         "roofline": roof,
         "forward_workloads": extra,
         "bias_workloads": bias_lines,
+        "mfma_rate_measured": None if measured is None else dict(
+            measured, unit="TFLOP/s",
+            note="pure 32x32 matrix-core products on pseudo-random operands, every CU, warm "
+                 "clock (fa_measure_mfma_rate): what the chip sustains within its power budget"),
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
     }

@@ -12,6 +12,8 @@ C names:
 * :func:`fa_bwd` -- dQ, dK, dV from Q, K, V, O, dO, LSE (and a workspace)
 * :func:`fa_bwd_delta`, :func:`fa_bwd_dkdv`, :func:`fa_bwd_dq` -- fa_bwd's three stages
 * :func:`fa_bwd_workspace_size`, :func:`fa_status_string`
+* :func:`fa_measure_mfma_rate` -- a measurement aid: the matrix-core rate on
+  realistic operand bits, against which the kernels' rates are also read
 
 There is no fallback: if the shared library is missing or fails to load, the
 import of :mod:`exact_io_aware_11_amd._lib` raises.
@@ -21,13 +23,13 @@ from __future__ import annotations
 from ._lib import (FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_FP32,
                    FA_FP8_E4M3, FA_OK, FAError, lib)
 from .api import (dtype_code, fa_bwd, fa_bwd_bias, fa_bwd_delta, fa_bwd_dkdv, fa_bwd_dq,
-                  fa_bwd_workspace_size, fa_fwd, fa_fwd_bias, fa_fwd_mxfp8, fa_status_string,
-                  flops_bwd, flops_fwd)
+                  fa_bwd_workspace_size, fa_fwd, fa_fwd_bias, fa_fwd_mxfp8, fa_measure_mfma_rate,
+                  fa_status_string, flops_bwd, flops_fwd)
 
 __all__ = [
     "FA_FP32", "FA_BF16", "FA_FP8_E4M3", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",
     "FA_ERR_HIP", "FAError", "lib", "fa_fwd", "fa_fwd_bias", "fa_fwd_mxfp8", "fa_bwd",
-    "fa_bwd_bias", "fa_bwd_delta", "fa_bwd_dkdv",
+    "fa_bwd_bias", "fa_bwd_delta", "fa_bwd_dkdv", "fa_measure_mfma_rate",
     "fa_bwd_dq", "fa_bwd_workspace_size",
     "fa_status_string", "dtype_code", "flops_fwd", "flops_bwd",
 ]

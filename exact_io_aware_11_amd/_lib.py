@@ -22,6 +22,7 @@ SIGNATURES = {
                          _i, _vp]),
     "fa_bwd_bias": (_i, [_vp, _vp, _vp, _vp, _ll, _ll, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _sz, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "fa_measure_mfma_rate": (_i, [_vp, _i, _i, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
 }
 for _stage in ("fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq"):

@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_bias", "fa_bwd_delta", "fa_bwd_dkdv",
                                     "fa_bwd_dq", "fa_bwd_workspace_size", "fa_fwd",
-                                    "fa_fwd_bias", "fa_fwd_mxfp8", "fa_status_string"]
+                                    "fa_fwd_bias", "fa_fwd_mxfp8", "fa_measure_mfma_rate",
+                                    "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -146,6 +147,14 @@ def test_bwd_rejects_before_launch(kw, status, fn):
 
 def test_bwd_empty_is_a_noop():
     assert bwd(N=0) == OK and bwd(B=0, q=0) == OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 256, 10, 1), INVALID), ((P + 2, 256, 10, 1), INVALID), ((P, 0, 10, 1), INVALID),
+    ((P, 65537, 10, 1), INVALID), ((P, 256, 0, 2), INVALID), ((P, 256, 1 << 21, 1), INVALID),
+    ((P, 256, 10, 0), UNSUPPORTED), ((P, 256, 10, 7), INVALID)])
+def test_rate_probe_rejects_before_launch(args, status):
+    assert lib.fa_measure_mfma_rate(*args, None) == status
 
 
 def test_workspace_size():
