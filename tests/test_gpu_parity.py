@@ -284,3 +284,14 @@ def test_many_heads_fwd_bwd():
             check(f"{tag} {name}", to_f64(got[sl]), ref, "bf16")
     for name, t in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
         assert torch.isfinite(t.float()).all(), name
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_rate_probe_runs(fp8):
+    """The matrix-core rate probe (a measurement aid) launches, writes every
+    output, and its FLOP count is the documented one."""
+    out = torch.full((4 * 512,), float("nan"), dtype=torch.float32, device="cuda")
+    flops = fa.fa_measure_mfma_rate(out, 4, 3, fp8)
+    torch.cuda.synchronize()
+    assert flops == 4 * 8 * 3 * 8 * (131072 if fp8 else 32768)
+    assert torch.isfinite(out).all()
