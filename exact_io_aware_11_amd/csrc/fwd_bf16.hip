@@ -41,9 +41,11 @@
 namespace fa {
 
 // (With a bias, one workgroup per CU: the bias of the tile after next is held
-// in registers for a whole step, which needs more than half the register file.)
+// in registers for a whole step, which needs more than half the register file.
+// At d = 64 without a bias, three workgroups per CU: 32 KiB of LDS each, and
+// the kernel fits in a third of the register file with a prefetch depth of 3.)
 template <int D, bool CAUSAL, int WAVES, bool BIAS>
-__global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : 8 / WAVES) void fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : (D == 64 ? 3 : 8 / WAVES)) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int N,
     uint32_t n_qblk, uint32_t total, float scale, float scale_log2, float grow_thr, Bias bias) {
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : 8 / WAVES) void fwd_
   // one) and row max of S_{j+1} over products 20-31, and this wave's share of
   // K_{j+2} and V_{j+1} is issued one load every 2 products early in the step,
   // so that it has landed by the next barrier.
-  constexpr int DEPTH = 4, NOPS = 2 * (D / 16) + 4 * (D / 32);
+  constexpr int DEPTH = D == 64 ? 3 : 4, NOPS = 2 * (D / 16) + 4 * (D / 32);
   constexpr int NS = 2 * (D / 16);  // S products come first
   auto step = [&](auto parity, auto maskc, int j) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;  // j % 2
