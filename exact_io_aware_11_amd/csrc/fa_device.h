@@ -54,20 +54,15 @@ __device__ __forceinline__ f32x16 mfma_fp8_scaled(i32x8 a, i32x8 b, f32x16 c, ui
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Workgroup barrier for the staged pipelines.  Before the barrier this wave's
-// LDS reads and writes are complete (lgkmcnt 0) and at most VM of its vector
-// memory operations -- the newest batch of direct HBM->LDS loads -- are still
-// in flight.  (__syncthreads() would also drain those loads: its workgroup
-// fence waits for vmcnt(0), which defeats prefetching.)  The "memory" clobber
-// keeps the compiler from moving memory accesses across the barrier.
-// Waitcnt immediate (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4]
-// (7: no wait), lgkmcnt [11:8] (0: wait for all).
 // Raw buffer resource over `bytes` bytes at `base`.  Buffer loads at byte
 // offsets past the end do not touch memory and deliver zeros (also into LDS),
 // which is how tiles running past the sequence end are padded.
+// num_records is a 32-bit unsigned field: byte counts up to 2^32 - 1 (callers
+// keep them below that) go in as their bit pattern.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  const uint32_t n = bytes > 0 ? (uint32_t)bytes : 0u;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           (int)(bytes > 0 ? bytes : 0), 0x00020000);
+                                           __builtin_bit_cast(int, n), 0x00020000);
 }
 // Loads into registers through a buffer resource (reads past num_records
 // return zeros): 16 or 4 bytes per lane at voff + soff + imm.
@@ -99,6 +94,14 @@ __device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, const void* 
                                            voff, 0, 0, 0);
 }
 
+// Workgroup barrier for the staged pipelines.  Before the barrier this wave's
+// LDS reads and writes are complete (lgkmcnt 0) and at most VM of its vector
+// memory operations -- the newest batch of direct HBM->LDS loads -- are still
+// in flight.  (__syncthreads() would also drain those loads: its workgroup
+// fence waits for vmcnt(0), which defeats prefetching.)  The "memory" clobber
+// keeps the compiler from moving memory accesses across the barrier.
+// Waitcnt immediate (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4]
+// (7: no wait), lgkmcnt [11:8] (0: wait for all).
 template <int VM>
 __device__ __forceinline__ void wait_vm() {
   static_assert(VM >= 0 && VM < 64, "vmcnt range");
