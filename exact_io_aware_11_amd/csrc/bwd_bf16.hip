@@ -25,8 +25,9 @@
 //
 // Optional additive bias (explainer V2 section: mask and bias merged into the
 // score stage): P = exp(scale S + bias - LSE); each tile's bias values are
-// loaded during the previous tile; rows whose LSE is -inf (no finite score in
-// the forward) get P = 0.
+// loaded during the previous tile (in the dQ pass they then become, as
+// bias / scale, the starting value of the S^T accumulators); rows whose LSE
+// is -inf (no finite score in the forward) get P = 0.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 }
 
 template <int D, bool CAUSAL, bool BIAS>
-__global__ __launch_bounds__(256, BIAS ? 1 : 2) void bwd_dq_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
@@ -410,14 +411,17 @@ __global__ __launch_bounds__(256, BIAS ? 1 : 2) void bwd_dq_bf16_kernel(
   const float del = qrow < N ? Delta[(size_t)bh * N + qrow] : 0.f;
   // Additive bias of this lane's query row: as in the forward, element i of
   // key half b of a tile at key0 is key key0 + 32 b + 8 (i / 4) + 4 g + i % 4,
-  // load x = 4 b + i / 4 of 16 bytes, component i % 4.
+  // load x = 4 b + i / 4 of 16 bytes, component i % 4.  A tile's bias is
+  // loaded during the previous tile's last product stream and, as bias /
+  // scale, becomes the starting value of the S^T accumulators, so it is not
+  // held while the softmax backward runs.
   [[maybe_unused]] const auto brs = BIAS ? bias_rsrc(bias, bh) : make_rsrc(nullptr, 0);
   [[maybe_unused]] const uint32_t bvoff =
       BIAS ? (uint32_t)((long long)min(qrow, N - 1) * bias.sq * 4 + 16 * g) : 0u;
-  [[maybe_unused]] f32x4 bv[2][8];  // [buffer][load]
-  auto load_bias = [&](auto bufc, int x, int key0) {
-    constexpr int BB = decltype(bufc)::value;
-    bv[BB][x] = buffer_load_f32x4(brs, bvoff + 128 * (x >> 2) + 32 * (x & 3), (uint32_t)key0 * 4u);
+  [[maybe_unused]] const float inv_scale = 1.f / scale;
+  [[maybe_unused]] f32x4 bv[8];
+  auto load_bias = [&](int x, int key0) {
+    bv[x] = buffer_load_f32x4(brs, bvoff + 128 * (x >> 2) + 32 * (x & 3), (uint32_t)key0 * 4u);
   };
 
   // K / V rows as A operands: row r32 (+32 b), chunk 2t + g.
@@ -500,16 +504,14 @@ __global__ __launch_bounds__(256, BIAS ? 1 : 2) void bwd_dq_bf16_kernel(
     auto op_a = [&](int b, int k, const bf16x8& a) {
       const int t = k >> 1;
       if (k & 1) dp[b] = mfma_bf16(a, of[t], t == 0 ? f32x16{} : dp[b]);
-      else s[b] = mfma_bf16(a, qf[t], t == 0 ? f32x16{} : s[b]);
+      else s[b] = mfma_bf16(a, qf[t], t == 0 && !BIAS ? f32x16{} : s[b]);
     };
     auto op_b = [&](int b, int k, const bf16x8& a) {
       const int h = k / NCB, cb = k % NCB;
       adq[cb] = mfma_bf16(a, db[b][h], adq[cb]);
     };
     auto soft_elem = [&](int b, int i) {  // key of element i: key0 + 32 b + 8 (i / 4) + 4 g + i % 4
-      float arg = -lse2;
-      if constexpr (BIAS) arg = fmaf(bv[BUF][4 * b + (i >> 2)][i & 3], kLog2e, arg);
-      float p = exp2_fast(fmaf(s[b][i], scale_log2, arg));
+      float p = exp2_fast(fmaf(s[b][i], scale_log2, -lse2));
       if constexpr (masked) {
         const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3);
         if ((CAUSAL && key > qrow) || (BIAS && key >= N)) p = 0.f;
@@ -536,7 +538,18 @@ __global__ __launch_bounds__(256, BIAS ? 1 : 2) void bwd_dq_bf16_kernel(
     auto stage_at = [&](int op) {
       if (op % SEV == 0 && op / SEV < 2 * LPW) stage_one(kr, vr, BN1{}, op / SEV);
     };
-    stream(false, 0, NA, [&](int k) { stage_at(k); });
+    auto init_bias = [&](int b, int i) { s[b][i] = bv[4 * b + (i >> 2)][i & 3] * inv_scale; };
+    if constexpr (BIAS) {  // half 0 starts from its bias now, half 1 during G_A(0)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) init_bias(0, i);
+    }
+    stream(false, 0, NA, [&](int k) {
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int i = k * 16 / NA; i < (k + 1) * 16 / NA; ++i) init_bias(1, i);
+      }
+      stage_at(k);
+    });
     stream(false, 1, NA, [&](int k) {
 #pragma unroll
       for (int i = k * 16 / NA; i < (k + 1) * 16 / NA; ++i) soft_elem(0, i);
@@ -550,7 +563,7 @@ __global__ __launch_bounds__(256, BIAS ? 1 : 2) void bwd_dq_bf16_kernel(
     if constexpr (BIAS) {  // the next tile's bias
       stream(true, 1, NB, [&](int k) {
 #pragma unroll
-        for (int x = k * 8 / NB; x < (k + 1) * 8 / NB; ++x) load_bias(BN1{}, x, key0 + BN);
+        for (int x = k * 8 / NB; x < (k + 1) * 8 / NB; ++x) load_bias(x, key0 + BN);
       });
     } else {
       stream(true, 1, NB, [](int) {});
@@ -571,7 +584,7 @@ __global__ __launch_bounds__(256, BIAS ? 1 : 2) void bwd_dq_bf16_kernel(
   }
   if constexpr (BIAS) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) load_bias(B0{}, x, 0);
+    for (int x = 0; x < 8; ++x) load_bias(x, 0);
   }
   int j = 0;
   for (; j + 2 <= j_full; j += 2) {

@@ -11,14 +11,14 @@
 // 4 waves handles a (batch, head, block of 128 query rows) -- under the causal
 // mask two blocks, u and n-1-u, one after the other, so that every workgroup
 // visits the same number of key tiles; each wave owns 32 query rows and scans
-// every visible key tile of 64 keys.
+// every visible key tile of 64 keys (32 with a bias at d = 128).
 //
 // gfx950 mapping:
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K (A operand) comes from LDS,
 //    Q (B operand) stays in registers for the whole scan.  In the C layout a
-//    lane then holds 16 keys of ONE query, so the row max is an in-lane max
-//    plus one exchange between the wave's halves (v_permlane32_swap), and the
-//    row sum needs no exchange until the end.
+//    lane then holds 16 keys of ONE query per 32-key half of a tile, so the
+//    row max is an in-lane max plus one exchange between the wave's halves
+//    (v_permlane32_swap), and the row sum needs no exchange until the end.
 //  * O^T = V^T P^T: the probabilities are converted to bf16 in place and used
 //    directly as the B operand (the C-layout key order is matched by reading
 //    V with ds_read_b64_tr_b16 in the same order); the accumulator then holds
@@ -28,11 +28,13 @@
 //    from HBM with 16-byte loads issued one tile ahead; one barrier per tile.
 //  * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA.
 //  * Optional additive bias (the explainer's V2 section merges mask and bias
-//    into the score stage): a tile's bias values are loaded one step before
-//    the step that uses them (16 bytes of four consecutive keys per load, two
-//    register buffers), so the per-step barrier's wait covers them, and added
-//    to the raw scores (as bias / scale) where the row max is taken; -inf
-//    masks.  A row that sees no finite score ends with O = 0 and LSE = -inf.
+//    into the score stage), -inf masking: a tile's bias (16 bytes of four
+//    consecutive keys per load) is loaded at the start of the step two before
+//    the one that forms its scores, and at the end of that step -- once the
+//    registers of the scores it will occupy are free -- becomes, as bias /
+//    scale, the starting value of the score accumulators.  Only one tile's
+//    bias is held at a time.  A row that sees no finite score ends with O = 0
+//    and LSE = -inf.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -40,17 +42,19 @@
 
 namespace fa {
 
-// (With a bias, one workgroup per CU: the bias of the tile after next is held
-// in registers for a whole step, which needs more than half the register file.
-// At d = 64 without a bias, three workgroups per CU: 32 KiB of LDS each, and
-// the kernel fits in a third of the register file with a prefetch depth of 3.)
+// Two workgroups per CU (64 KiB of LDS and at most 256 registers per wave); at
+// d = 64 without a bias three (32 KiB of LDS each; the kernel fits in a third
+// of the register file with a prefetch depth of 3).  A bias at d = 128 takes
+// 32-key tiles: two 64-key score tiles and a tile's bias do not fit in the
+// registers of two workgroups per CU, one 32-key score tile less does.
 template <int D, bool CAUSAL, int WAVES, bool BIAS>
-__global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : (D == 64 ? 3 : 8 / WAVES)) void fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int N,
     uint32_t n_qblk, uint32_t total, float scale, float scale_log2, float grow_thr, Bias bias) {
-  constexpr int BM = 32 * WAVES, BN = 64, TILE = BN * D;  // TILE: elements of one K or V tile
-  constexpr int LPW = TILE * 2 / 1024 / WAVES;            // 1 KiB direct loads per wave per tile
+  constexpr int BM = 32 * WAVES, BN = BIAS && D == 128 ? 32 : 64;
+  constexpr int NH = BN / 32, TILE = BN * D;  // NH: 32-key halves per tile; TILE: elements of a K or V tile
+  constexpr int LPW = TILE * 2 / 1024 / WAVES;  // 1 KiB direct loads per wave per tile
   // Two K and two V tile buffers as four separate arrays: the compiler tells
   // LDS variables apart, so reading one buffer does not wait for the direct
   // loads that are still filling another.
@@ -89,20 +93,26 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : (D == 64 ? 3 : 8 / W
 
   // Additive bias: a buffer resource over this (b, h) slice and the byte
   // offset of this lane's row (rows past N read row N - 1; they are never
-  // written).  Element i of key half b of a tile at key0 is key
-  // key0 + 32 b + 8 (i / 4) + 4 g + i % 4: load x = 4 b + i / 4, component i % 4.
+  // written).  Element i of key half h of a tile at key0 is key
+  // key0 + 32 h + 8 (i / 4) + 4 g + i % 4: load x = 4 h + i / 4, component i % 4.
   [[maybe_unused]] const auto brs = BIAS ? bias_rsrc(bias, bh) : make_rsrc(nullptr, 0);
   [[maybe_unused]] const uint32_t bvoff =
       BIAS ? (uint32_t)((long long)min(qrow, N - 1) * bias.sq * 4 + 16 * g) : 0u;
   [[maybe_unused]] const float inv_scale = 1.f / scale;
-  auto load_bias = [&](f32x4 (&bv)[8], int key0) __attribute__((always_inline)) {
+  auto load_bias = [&](f32x4 (&bv)[4 * NH], int key0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x)
+    for (int x = 0; x < 4 * NH; ++x)
       bv[x] = buffer_load_f32x4(brs, bvoff + 128 * (x >> 2) + 32 * (x & 3), (uint32_t)key0 * 4u);
   };
-  auto add_bias = [&](const f32x4 (&bv)[8], f32x16& s0, f32x16& s1, int i) __attribute__((always_inline)) {
-    s0[i] = fmaf(bv[i >> 2][i & 3], inv_scale, s0[i]);
-    s1[i] = fmaf(bv[4 + (i >> 2)][i & 3], inv_scale, s1[i]);
+  auto add_bias = [&](const f32x4 (&bv)[4 * NH], f32x16 (&s)[NH], int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) s[h][i] = fmaf(bv[4 * h + (i >> 2)][i & 3], inv_scale, s[h][i]);
+  };
+  // The bias in raw-score units as the starting value of a tile's score
+  // accumulators: the matrix core then adds K Q^T to it.
+  auto init_bias = [&](const f32x4 (&bv)[4 * NH], f32x16 (&s)[NH], int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) s[h][i] = bv[4 * h + (i >> 2)][i & 3] * inv_scale;
   };
 
   // Q fragment as the B operand of S^T = K Q^T: lane holds Q[qrow][16t + 8g .. +7].
@@ -118,7 +128,7 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : (D == 64 ? 3 : 8 / W
 
   // Per-lane element offsets inside one tile buffer (the swizzle depends only
   // on row % 16, so whole 16-row steps are plain constants added to these).
-  int koff[D / 16];  // K as the A operand: row r32 (+32b), chunk 2t + g
+  int koff[D / 16];  // K as the A operand: row r32 (+32h), chunk 2t + g
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) koff[t] = tile_off<D>(r32, 2 * t + g);
   // V by the transposing read: source lane (r, c) = ((lane%16)/4, lane%4) reads
@@ -166,40 +176,31 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : (D == 64 ? 3 : 8 / W
     else return -m_run * scale_log2;
   };
 
-  auto scores = [&](const uint16_t* Kt, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
-    s0 = mfma_bf16(lds_read_b128(Kt + koff[0]), qf[0], f32x16{});
-    s1 = mfma_bf16(lds_read_b128(Kt + 32 * D + koff[0]), qf[0], f32x16{});
+  auto scores = [&](const uint16_t* Kt, f32x16 (&s)[NH]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 1; t < D / 16; ++t) {
-      s0 = mfma_bf16(lds_read_b128(Kt + koff[t]), qf[t], s0);
-      s1 = mfma_bf16(lds_read_b128(Kt + 32 * D + koff[t]), qf[t], s1);
-    }
+    for (int h = 0; h < NH; ++h) s[h] = mfma_bf16(lds_read_b128(Kt + 32 * D * h + koff[0]), qf[0], f32x16{});
+#pragma unroll
+    for (int t = 1; t < D / 16; ++t)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) s[h] = mfma_bf16(lds_read_b128(Kt + 32 * D * h + koff[t]), qf[t], s[h]);
   };
 
-  // Online softmax of tile j's scores, then O^T += V_j^T P_j^T.
   // O^T += V_j^T P_j^T with P_j in bf16 (the B operand exactly as the
-  // accumulator layout left it; V read transposed in the same key order).
-  auto pv = [&](const uint16_t* Vt, bf16x8 p00, bf16x8 p01, bf16x8 p10, bf16x8 p11) __attribute__((always_inline)) {
+  // accumulator layout left it, one operand per 16-key chunk; V read
+  // transposed in the same key order).
+  auto pv = [&](const uint16_t* Vt, const bf16x8 (&p)[2 * NH]) __attribute__((always_inline)) {
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) {
       const uint16_t* vb = Vt + voff[cb][0];
       const uint16_t* vc = Vt + voff[cb][1];
-      acc[cb] = mfma_bf16(concat(lds_read_tr16(vb), lds_read_tr16(vc)), p00, acc[cb]);
-      acc[cb] = mfma_bf16(concat(lds_read_tr16(vb + 16 * D), lds_read_tr16(vc + 16 * D)), p01, acc[cb]);
-      acc[cb] = mfma_bf16(concat(lds_read_tr16(vb + 32 * D), lds_read_tr16(vc + 32 * D)), p10, acc[cb]);
-      acc[cb] = mfma_bf16(concat(lds_read_tr16(vb + 48 * D), lds_read_tr16(vc + 48 * D)), p11, acc[cb]);
+#pragma unroll
+      for (int kc = 0; kc < 2 * NH; ++kc)
+        acc[cb] = mfma_bf16(concat(lds_read_tr16(vb + 16 * D * kc), lds_read_tr16(vc + 16 * D * kc)),
+                            p[kc], acc[cb]);
     }
   };
 
-  // Online softmax (FA1 page 10.2.2; reading notes code 3-1) against a
-  // running reference max m_run.  Lazy rescale: m_run only moves when some
-  // row's tile max exceeds it by more than grow_thr (2^16 in probability);
-  // the accumulator and row sum are then rescaled by alpha = exp(m_old -
-  // m_new).  Otherwise the probabilities exp(S - m_run) may reach 2^16,
-  // which float32 accumulation and bf16 P hold exactly as well as values <= 1
-  // -- any reference gives the same exact result.  The first tile always
-  // moves m_run off -infinity.
-  // Rescale to a new reference max (rare; see rowmax_guard).
+  // Rescale to a new reference max (rare; see guard).
   auto rescale = [&](float mx) __attribute__((always_inline)) {
     const float m_new = fmaxf(m_run, mx);
     float alpha = exp2_fast((m_run - m_new) * scale_log2);
@@ -223,38 +224,41 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : (D == 64 ? 3 : 8 / W
     mx = halves_max(mx);
     if (__builtin_amdgcn_ballot_w64(mx > m_run + grow_thr) != 0) rescale(mx);
   };
-  auto rowmax_guard = [&](const f32x16& s0, const f32x16& s1) __attribute__((always_inline)) {
-    float mx = fmaxf(s0[0], s1[0]);
+  auto rowmax_guard = [&](const f32x16 (&s)[NH]) __attribute__((always_inline)) {
+    float mx = NH == 2 ? fmaxf(s[0][0], s[NH - 1][0]) : s[0][0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, NH == 2 ? fmaxf(s[0][i], s[NH - 1][i]) : s[0][i]);
     guard(mx);
   };
   // P = exp(S - m_run) in place; row sum over the float32 P; P in bf16 out.
-  auto exps = [&](f32x16& s0, f32x16& s1, bf16x8& p00, bf16x8& p01, bf16x8& p10,
-                  bf16x8& p11) __attribute__((always_inline)) {
+  auto exps = [&](f32x16 (&s)[NH], bf16x8 (&p)[2 * NH]) __attribute__((always_inline)) {
     const float mneg = neg_ref();
-    float rs0 = 0.f, rs1 = 0.f;
+    float rs[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) rs[h] = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s0[i] = exp2_fast(fmaf(s0[i], scale_log2, mneg));
-      s1[i] = exp2_fast(fmaf(s1[i], scale_log2, mneg));
-      rs0 += s0[i];
-      rs1 += s1[i];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) s[h][i] = exp2_fast(fmaf(s[h][i], scale_log2, mneg));
+#pragma unroll
+      for (int h = 0; h < NH; ++h) rs[h] += s[h][i];
     }
-    l_run += rs0 + rs1;
-    p00 = to_bf16x8(s0, 0);
-    p01 = to_bf16x8(s0, 8);
-    p10 = to_bf16x8(s1, 0);
-    p11 = to_bf16x8(s1, 8);
+    l_run += NH == 2 ? rs[0] + rs[NH - 1] : rs[0];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      p[2 * h] = to_bf16x8(s[h], 0);
+      p[2 * h + 1] = to_bf16x8(s[h], 8);
+    }
   };
 
   // Masked scores: keys past N, and under the causal mask keys after the query.
-  auto apply_mask = [&](f32x16& s0, f32x16& s1, int key0) __attribute__((always_inline)) {
+  auto apply_mask = [&](f32x16 (&s)[NH], int key0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = key0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (key >= N || (CAUSAL && key > qrow)) s0[i] = -INFINITY;
-      if (key + 32 >= N || (CAUSAL && key + 32 > qrow)) s1[i] = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        if (key + 32 * h >= N || (CAUSAL && key + 32 * h > qrow)) s[h][i] = -INFINITY;
     }
   };
 
@@ -265,53 +269,53 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : (D == 64 ? 3 : 8 / W
   // their scores are formed.  The two score buffers swap roles with the step
   // parity, so nothing is copied.
   const int j_full = min(CAUSAL ? (int)qblk * (BM / BN) : n_tiles, N / BN);
-  f32x16 sa0, sa1, sb0, sb1;  // scores of even (a) and odd (b) tiles, two key halves each
-  auto sc_lo = [&](auto parity) __attribute__((always_inline)) -> f32x16& {
-    if constexpr (decltype(parity)::value == 0) return sa0;
-    else return sb0;
+  f32x16 sa[NH], sb[NH];  // scores of even (a) and odd (b) tiles, by key half
+  auto sc_of = [&](auto parity) __attribute__((always_inline)) -> f32x16 (&)[NH] {
+    if constexpr (decltype(parity)::value == 0) return sa;
+    else return sb;
   };
-  auto sc_hi = [&](auto parity) __attribute__((always_inline)) -> f32x16& {
-    if constexpr (decltype(parity)::value == 0) return sa1;
-    else return sb1;
-  };
+  // Bias of tile t + 1: loaded at the start of step t - 1 (tiles 0 and 1
+  // here) and turned into the starting value of S_{t+1} at the end of that
+  // step, once P_{t-1} no longer needs the registers S_{t+1} will use.
+  [[maybe_unused]] f32x4 bv0[4 * NH], bv[4 * NH];
+  if constexpr (BIAS) {
+    load_bias(bv0, 0);
+    load_bias(bv, BN);
+  }
   stage(Kh, lk0, 0);
   stage(Vh, lv0, 0);
   barrier_vm<0>();
   stage(Kh, lk1, BN);  // (a tile past the end arrives as zeros; never used)
-  // bias of tile t lives in bvb[t % 2] from the step before it is used
-  [[maybe_unused]] f32x4 bvb[2][8];
+  scores(lk0, sa);
   if constexpr (BIAS) {
-    f32x4 bv0[8];
-    load_bias(bv0, 0);
-    load_bias(bvb[1], BN);
-    scores(lk0, sa0, sa1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) add_bias(bv0, sa0, sa1, i);
-  } else {
-    scores(lk0, sa0, sa1);
+    for (int i = 0; i < 16; ++i) {
+      add_bias(bv0, sa, i);
+      init_bias(bv, sb, i);
+    }
   }
-  if (j_full == 0) apply_mask(sa0, sa1, 0);
-  rowmax_guard(sa0, sa1);
+  if (j_full == 0) apply_mask(sa, 0);
+  rowmax_guard(sa);
 
-  // Step j < n_tiles - 1: one fenced stream of 32 matrix products,
-  // S_{j+1} = K_{j+1} Q^T (16, K from LDS) then O^T += V_j^T P_j^T (16, V by
-  // the transposing read, key chunk by key chunk), every operand fetched
-  // DEPTH products ahead.  The vector work rides between the products: exp,
-  // row sum and bf16 packing of P_j over products 0-23 (each key chunk of P
-  // is complete before its first PV product), the mask (when tile j+1 needs
-  // one) and row max of S_{j+1} over products 20-31, and this wave's share of
-  // K_{j+2} and V_{j+1} is issued one load every 2 products early in the step,
-  // so that it has landed by the next barrier.
-  constexpr int DEPTH = D == 64 ? 3 : 4, NOPS = 2 * (D / 16) + 4 * (D / 32);
-  constexpr int NS = 2 * (D / 16);  // S products come first
+  // Step j < n_tiles - 1: one fenced stream of matrix products,
+  // S_{j+1} = K_{j+1} Q^T (NS products, K from LDS) then O^T += V_j^T P_j^T
+  // (V by the transposing read, key chunk by key chunk), every operand
+  // fetched DEPTH products ahead.  The vector work rides between the
+  // products: exp, row sum and bf16 packing of P_j over the first EXP_OPS + 2
+  // products (each key chunk of P is complete before its first PV product),
+  // the mask (when tile j+1 needs one) and row max of S_{j+1} over the last
+  // MAX_OPS products, with a bias the starting value of S_{j+2} once P_j is
+  // packed, and this wave's share of K_{j+2} and V_{j+1} issued one load every
+  // 2 products early in the step, so that it has landed by the next barrier.
+  constexpr int DEPTH = D == 64 ? 3 : 4;
+  constexpr int NS = NH * (D / 16), NOPS = NS + 2 * NH * (D / 32);  // S products come first
+  constexpr int EXP_OPS = NH == 2 ? NS + 2 * (D / 32) : NS + 2, MAX_OPS = NH == 2 ? 12 : 4;
   auto step = [&](auto parity, auto maskc, int j) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;  // j % 2
     constexpr bool MASK_NEXT = decltype(maskc)::value;
     using PN = std::integral_constant<int, P ^ 1>;
-    f32x16& sc0 = sc_lo(parity);
-    f32x16& sc1 = sc_hi(parity);
-    f32x16& sn0 = sc_lo(PN{});
-    f32x16& sn1 = sc_hi(PN{});
+    f32x16(&sc)[NH] = sc_of(parity);
+    f32x16(&sn)[NH] = sc_of(PN{});
     barrier_vm<0>();  // this wave's pieces of K_{j+1} and V_j have landed, and everyone's
     const uint16_t* Kt = ktile(PN{});
     const uint16_t* Vt = vtile(parity);
@@ -319,38 +323,35 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : (D == 64 ? 3 : 8 / W
     uint16_t* Kdst = ktile(parity);
     const float mneg = neg_ref();
     const int key1 = (j + 1) * BN;
-    // bias: tile j + 1's (used below) arrived during step j - 1; tile j + 2's
-    // goes into the buffer tile j's used, ahead of this step's staging loads
-    [[maybe_unused]] f32x4(&bv)[8] = bvb[P ^ 1];
-    if constexpr (BIAS) load_bias(bvb[P], key1 + BN);
+    // tile j + 2's bias, ahead of this step's staging loads
+    if constexpr (BIAS) load_bias(bv, key1 + BN);
     const auto kres = tile_rsrc(Kh, (j + 2) * BN);
     const auto vres = tile_rsrc(Vh, (j + 1) * BN);
-    bf16x8 pk[4];
+    bf16x8 pk[2 * NH];
     auto fetch = [&](int k) __attribute__((always_inline)) -> bf16x8 {
-      if (k < NS) return lds_read_b128(Kt + 32 * D * (k & 1) + koff[k >> 1]);
+      if (k < NS) return lds_read_b128(Kt + 32 * D * (k % NH) + koff[k / NH]);
       const int kc = (k - NS) / (D / 32), cb = (k - NS) % (D / 32);
       return concat(lds_read_tr16(Vt + voff[cb][0] + 16 * D * kc),
                     lds_read_tr16(Vt + voff[cb][1] + 16 * D * kc));
     };
     auto op = [&](int k, const bf16x8& a) __attribute__((always_inline)) {
       if (k < NS) {
-        const int t = k >> 1;
-        if (k & 1) sn1 = mfma_bf16(a, qf[t], t == 0 ? f32x16{} : sn1);
-        else sn0 = mfma_bf16(a, qf[t], t == 0 ? f32x16{} : sn0);
+        const int t = k / NH, h = k % NH;
+        sn[h] = mfma_bf16(a, qf[t], t == 0 && !BIAS ? f32x16{} : sn[h]);
       } else {
         const int kc = (k - NS) / (D / 32), cb = (k - NS) % (D / 32);
         acc[cb] = mfma_bf16(a, pk[kc], acc[cb]);
       }
     };
-    // Element e of P_j (s0[0..15], then s1[0..15]) in three phases placed in
-    // three consecutive products, so that no instruction waits on the one
-    // just before it: (a) the scaled, shifted score; (b) its exp; (c) the row
-    // sum (two partial sums) and, closing a key chunk, the bf16 packing.  The
-    // empty volatile statements pin each phase to its product.
+    // Element e of P_j (key half e / 16, element e % 16) in three phases
+    // placed in three consecutive products, so that no instruction waits on
+    // the one just before it: (a) the scaled, shifted score; (b) its exp; (c)
+    // the row sum (two partial sums) and, closing a key chunk, the bf16
+    // packing.  The empty volatile statements pin each phase to its product.
     float lsum[2] = {0.f, 0.f};
     auto pin = [](float& x) __attribute__((always_inline)) { asm volatile("" : "+v"(x)); };
     auto phase = [&](int e, int ph) __attribute__((always_inline)) {
-      f32x16& sv = (e < 16) ? sc0 : sc1;
+      f32x16& sv = sc[e >> 4];
       const int i = e & 15;
       float x = sv[i];
       if (ph == 0) {
@@ -366,18 +367,15 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : (D == 64 ? 3 : 8 / W
       sv[i] = x;
       if (ph == 2 && (e & 7) == 7) pk[e >> 3] = to_bf16x8(sv, i - 7);
     };
-    auto mask_next = [&](int i) __attribute__((always_inline)) {  // element i of both halves of S_{j+1}
-      if constexpr (BIAS) add_bias(bv, sn0, sn1, i);
-      if constexpr (MASK_NEXT) {
-        const int key = key1 + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (key >= N || (CAUSAL && key > qrow)) sn0[i] = -INFINITY;
-        if (key + 32 >= N || (CAUSAL && key + 32 > qrow)) sn1[i] = -INFINITY;
-      }
+    auto mask_next = [&](int i) __attribute__((always_inline)) {  // element i of each half of S_{j+1}
+      const int key = key1 + 8 * (i >> 2) + 4 * g + (i & 3);
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        if (key + 32 * h >= N || (CAUSAL && key + 32 * h > qrow)) sn[h][i] = -INFINITY;
     };
     // Elements start phase (a) over products 0 .. EXP_OPS-1; phase (c) of the
     // last element of key chunk kc lands two products later, before product
     // NS + kc (D/32), the chunk's first PV product.
-    constexpr int EXP_OPS = NS + 2 * (D / 32);
     float mxp[2] = {-INFINITY, -INFINITY};
     auto extra = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
@@ -385,16 +383,24 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : (D == 64 ? 3 : 8 / W
         const int ks = k - ph;
         if (ks >= 0 && ks < EXP_OPS) {
 #pragma unroll
-          for (int e = ks * 32 / EXP_OPS; e < (ks + 1) * 32 / EXP_OPS; ++e) phase(e, ph);
+          for (int e = ks * 16 * NH / EXP_OPS; e < (ks + 1) * 16 * NH / EXP_OPS; ++e) phase(e, ph);
         }
       }
-      if (k >= NOPS - 12) {  // row max of S_{j+1}, 32 values over the last 12 products
-        const int r = k - (NOPS - 12);
+      if (k >= NOPS - MAX_OPS) {  // row max of S_{j+1} over the last MAX_OPS products
+        const int r = k - (NOPS - MAX_OPS);
 #pragma unroll
-        for (int i = r * 16 / 12; i < (r + 1) * 16 / 12; ++i) {
-          if constexpr (MASK_NEXT || BIAS) mask_next(i);
-          mxp[i & 1] = fmaxf(mxp[i & 1], fmaxf(sn0[i], sn1[i]));
+        for (int i = r * 16 / MAX_OPS; i < (r + 1) * 16 / MAX_OPS; ++i) {
+          if constexpr (MASK_NEXT) mask_next(i);
+          mxp[i & 1] = fmaxf(mxp[i & 1], NH == 2 ? fmaxf(sn[0][i], sn[NH - 1][i]) : sn[0][i]);
           pin(mxp[i & 1]);
+        }
+      }
+      if constexpr (BIAS) {  // S_{j+2} starts from its bias, once P_j is packed
+        constexpr int K0 = EXP_OPS + 2, NI = NOPS - K0;
+        static_assert(NI > 0, "no product left after the exp phases");
+        if (k >= K0) {
+#pragma unroll
+          for (int i = (k - K0) * 16 / NI; i < (k - K0 + 1) * 16 / NI; ++i) init_bias(bv, sc, i);
         }
       }
       if (k % 2 == 0 && k / 2 < 2 * LPW) {  // loads: K_{j+2} pieces, then V_{j+1}
@@ -419,11 +425,10 @@ __global__ __launch_bounds__(64 * WAVES, BIAS ? 4 / WAVES : (D == 64 ? 3 : 8 / W
   };
   // Last tile: no next scores; P_j then O^T += V_j^T P_j^T.
   auto step_last = [&](auto parity) __attribute__((always_inline)) {
-    constexpr int P = decltype(parity)::value;
     barrier_vm<0>();
-    bf16x8 p00, p01, p10, p11;
-    exps(sc_lo(parity), sc_hi(parity), p00, p01, p10, p11);
-    pv(vtile(parity), p00, p01, p10, p11);
+    bf16x8 p[2 * NH];
+    exps(sc_of(parity), p);
+    pv(vtile(parity), p);
   };
   // Steps whose next tile is full, then the rest (masking the next tile's
   // scores is correct for any tile, just slower), then the last tile.
