@@ -2,8 +2,8 @@
 """Benchmark of the attention hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input: the
-forward (fa_fwd) and the three backward stages (fa_bwd_delta, fa_bwd_dkdv,
-fa_bwd_dq -- exactly what fa_bwd enqueues), on the bf16 causal workload
+forward (fa_fwd) and the backward stages (fa_bwd_dq, which also forms delta,
+then fa_bwd_dkdv -- exactly what fa_bwd enqueues for bf16), on the bf16 causal workload
 B=2, H=16, N=4096, d=128 unless --workload says otherwise.  Inputs are resident
 in device memory before the timed region starts.  Each kernel is bracketed by
 HIP events on the stream it runs on, so per-kernel durations are measured live.
@@ -120,6 +120,7 @@ def algorithmic_work(w):
     return {
         "fwd": fa.flops_fwd(B, H, N, d, c),
         # dK/dV kernel: S recompute, dV, dP, dK; dQ kernel: the dQ product
+        # (its S and dP recomputes, and for bf16 delta, are not counted)
         "dkdv": 4 * per_product,
         "dq": 1 * per_product,
         # delta kernel: reads O and dO, writes one float per row
@@ -157,7 +158,10 @@ def time_main(w, steps, warmup, warm_s=0.0):
     if w.backward:
         dq, dk, dv = (torch.empty_like(q) for _ in range(3))
         ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device="cuda")
-    stages = ["fwd"] + (["delta", "dkdv", "dq"] if w.backward else [])
+    # the stages fa_bwd enqueues: for bf16 the dQ kernel forms delta itself
+    bwd_stages = ["dq", "dkdv"] if w.dtype == "bf16" else ["delta", "dkdv", "dq"]
+    stages = ["fwd"] + (bwd_stages if w.backward else [])
+    calls = {"delta": fa.fa_bwd_delta, "dkdv": fa.fa_bwd_dkdv, "dq": fa.fa_bwd_dq}
 
     def step(ev):
         ev[0].record()
@@ -165,12 +169,9 @@ def time_main(w, steps, warmup, warm_s=0.0):
         ev[1].record()
         if w.backward:
             args = (q, k, v, o, do, lse, dq, dk, dv, ws, w.scale, w.causal)
-            fa.fa_bwd_delta(*args)
-            ev[2].record()
-            fa.fa_bwd_dkdv(*args)
-            ev[3].record()
-            fa.fa_bwd_dq(*args)
-            ev[4].record()
+            for i, s in enumerate(stages[1:]):
+                calls[s](*args)
+                ev[i + 2].record()
 
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]

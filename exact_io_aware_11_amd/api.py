@@ -210,19 +210,22 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale: float, causal: b
 
 
 def fa_bwd_delta(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream=None):
-    """Stage 1 of fa_bwd: delta into the workspace."""
+    """Backward stage: delta into the workspace (fa_bwd runs it for float32;
+    for bf16 the dQ stage forms delta itself)."""
     _bwd_call("fa_bwd_delta", q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal,
               stream)
 
 
 def fa_bwd_dkdv(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream=None):
-    """Stage 2 of fa_bwd: dK and dV."""
+    """Backward stage: dK and dV, reading delta from the workspace."""
     _bwd_call("fa_bwd_dkdv", q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal,
               stream)
 
 
 def fa_bwd_dq(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream=None):
-    """Stage 3 of fa_bwd: dQ."""
+    """Backward stage: dQ (bf16: also writes delta to the workspace; float32:
+    reads it).  fa_bwd is fa_bwd_dq then fa_bwd_dkdv for bf16, and
+    fa_bwd_delta, fa_bwd_dkdv, fa_bwd_dq for float32."""
     _bwd_call("fa_bwd_dq", q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream)
 
 

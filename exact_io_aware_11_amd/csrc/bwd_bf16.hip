@@ -7,7 +7,7 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),
 //   dK = scale dS^T Q,  dQ = scale dS K.
 //
-// Two kernels after the delta kernel, on one stream, no atomics:
+// Two kernels on one stream, dQ first, no atomics:
 //  * dK/dV: one workgroup per (batch, head, block of 128 keys); each wave
 //    holds 32 keys' K and V rows in registers and scans the query tiles of 64
 //    rows that can see them (all, or those at or after the keys when causal).
@@ -19,7 +19,8 @@
 //    holds 32 queries' Q and dO rows in registers and scans the key tiles.
 //    S^T = K Q^T and dP^T = V dO^T give one query per lane column (so LSE and
 //    delta are per-lane scalars); dS^T feeds dQ^T = K^T dS^T with K^T read by
-//    the transposing LDS read.
+//    the transposing LDS read.  It forms delta from its rows of O and dO and
+//    stores it for the dK/dV kernel, so no separate delta pass is needed.
 // Recomputing S and dP in the dQ pass costs two extra matrix products over
 // the five the method needs; it keeps every output written exactly once.
 //
@@ -359,8 +360,9 @@ template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
-    int N, uint32_t n_qblk, uint32_t total, float scale, float scale_log2, Bias bias) {
+    const uint16_t* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ Delta,
+    uint16_t* __restrict__ dQ, int N, uint32_t n_qblk, uint32_t total, float scale,
+    float scale_log2, Bias bias) {
   constexpr int BM = 128, BN = 64, TILE = BN * D;
   constexpr int LPW = TILE * 2 / 1024 / 4;  // 1 KiB direct loads per wave per tile and tensor
   constexpr int NT = D / 16, NCB = D / 32;
@@ -408,7 +410,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   // +inf, so that their P is exactly 0 whatever the bias there.)
   float lse2 = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
   if constexpr (BIAS) lse2 = (qrow < N && lse2 != -__builtin_inff()) ? lse2 : __builtin_inff();
-  const float del = qrow < N ? Delta[(size_t)bh * N + qrow] : 0.f;
+  // delta_i = sum_c dO_ic O_ic (FA1 page, section 10.2.4): the lane holds
+  // head dims 16t + 8g .. +7 of its query's dO row; it reads the same part of
+  // O, and the wave's two halves add their partial sums.  Stored for the
+  // dK/dV pass, which runs after this one.
+  float del;
+  {
+    float part = 0.f;
+    if (qrow < N) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(O + head + (size_t)qrow * D + 16 * t + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf((float)o8[e], (float)of[t][e], part);
+      }
+    }
+    del = halves_sum(part);
+    if (qrow < N && g == 0) Delta[(size_t)bh * N + qrow] = del;
+  }
   // Additive bias of this lane's query row: as in the forward, element i of
   // key half b of a tile at key0 is key key0 + 32 b + 8 (i / 4) + 4 g + i % 4,
   // load x = 4 b + i / 4 of 16 bytes, component i % 4.  A tile's bias is
@@ -628,8 +647,8 @@ static hipError_t dq_bf16_t(const BwdArgs& a) {
   const uint32_t total = (uint32_t)(a.BH * n_qblk);
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, BIAS>), dim3(total), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.N, n_qblk,
-                     total, a.scale, a.scale * kLog2e, a.bias);
+                     (const uint16_t*)a.dout, (const uint16_t*)a.o, a.lse, a.delta,
+                     (uint16_t*)a.dq, a.N, n_qblk, total, a.scale, a.scale * kLog2e, a.bias);
   return hipGetLastError();
 }
 

@@ -204,12 +204,18 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   a.causal = causal != 0;
   a.bias = bias;
   a.stream = (hipStream_t)stream;
-  const bool bf16 = dtype == FA_BF16;
   hipError_t e = hipSuccess;
-  if (stages & kStageDelta) e = fa::launch_delta(a, bf16);
-  if (e == hipSuccess && (stages & kStageDkDv))
-    e = bf16 ? fa::launch_dkdv_bf16(a) : fa::launch_dkdv_f32(a);
-  if (e == hipSuccess && (stages & kStageDq)) e = bf16 ? fa::launch_dq_bf16(a) : fa::launch_dq_f32(a);
+  if (dtype == FA_BF16) {
+    // The bf16 dQ kernel forms delta itself and stores it for the dK/dV
+    // kernel: dQ runs first and a full backward needs no delta launch.
+    if ((stages & kStageDelta) && !(stages & kStageDq)) e = fa::launch_delta(a, true);
+    if (e == hipSuccess && (stages & kStageDq)) e = fa::launch_dq_bf16(a);
+    if (e == hipSuccess && (stages & kStageDkDv)) e = fa::launch_dkdv_bf16(a);
+  } else {
+    if (stages & kStageDelta) e = fa::launch_delta(a, false);
+    if (e == hipSuccess && (stages & kStageDkDv)) e = fa::launch_dkdv_f32(a);
+    if (e == hipSuccess && (stages & kStageDq)) e = fa::launch_dq_f32(a);
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

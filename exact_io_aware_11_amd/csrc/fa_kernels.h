@@ -65,7 +65,7 @@ hipError_t launch_delta(const BwdArgs& a, bool bf16);
 hipError_t launch_dkdv_f32(const BwdArgs& a);
 hipError_t launch_dq_f32(const BwdArgs& a);
 hipError_t launch_dkdv_bf16(const BwdArgs& a);
-hipError_t launch_dq_bf16(const BwdArgs& a);
+hipError_t launch_dq_bf16(const BwdArgs& a);  // also writes delta (from O and dO)
 hipError_t launch_mfma_peak(float* out, int blocks, int iters, bool fp8, hipStream_t stream);
 
 }  // namespace fa

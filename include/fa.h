@@ -136,16 +136,18 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
                  int dtype, void* stream);
 
-/* The three stages fa_bwd enqueues, in its order, with fa_bwd's arguments and
- * validation (each stage uses the pointers it needs; the others must still be
- * valid).  fa_bwd(...) is exactly fa_bwd_delta(...); fa_bwd_dkdv(...);
- * fa_bwd_dq(...) on one stream.  They let a caller schedule or time the stages
- * separately.
+/* The backward's stages, with fa_bwd's arguments and validation (each stage
+ * uses the pointers it needs; the others must still be valid).  They let a
+ * caller schedule or time the stages separately.
  *   fa_bwd_delta : delta_i = dO_i . O_i into the workspace (FA1 page, 10.2.4)
+ *   fa_bwd_dq    : dQ.  FA_BF16: it also forms delta from O and dO itself and
+ *                  writes it into the workspace; FA_FP32: it reads delta from
+ *                  the workspace
  *   fa_bwd_dkdv  : dK and dV, reading delta from the workspace
- *   fa_bwd_dq    : dQ, reading delta from the workspace
- * dkdv and dq need a delta written earlier on the same stream (or made
- * visible by the caller's synchronisation). */
+ * fa_bwd(...) is exactly, on one stream, fa_bwd_dq(...); fa_bwd_dkdv(...) for
+ * FA_BF16 and fa_bwd_delta(...); fa_bwd_dkdv(...); fa_bwd_dq(...) for FA_FP32.
+ * A stage that reads delta needs it written earlier on the same stream (or
+ * made visible by the caller's synchronisation). */
 fa_status fa_bwd_delta(const void* q, const void* k, const void* v, const void* o,
                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
                        void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
@@ -163,7 +165,7 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, 
  * exp(scale q.k + bias - LSE) from the LSE that fa_fwd_bias wrote (rows with
  * LSE = -inf have P = 0 and add nothing).  The bias is an input: no gradient
  * is formed for it.  Arguments as fa_bwd plus the bias of fa_fwd_bias;
- * enqueues the delta, dK/dV and dQ kernels.  FA_FP8_E4M3 returns
+ * enqueues the same stages as fa_bwd.  FA_FP8_E4M3 returns
  * FA_ERR_UNSUPPORTED. */
 fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const float* bias,
                       long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
