@@ -10,7 +10,8 @@ C names:
 * :func:`fa_fwd_bias`, :func:`fa_bwd_bias` -- forward and backward with an
   additive bias (and masks, as -inf) on the scaled scores
 * :func:`fa_bwd` -- dQ, dK, dV from Q, K, V, O, dO, LSE (and a workspace)
-* :func:`fa_bwd_delta`, :func:`fa_bwd_dkdv`, :func:`fa_bwd_dq` -- fa_bwd's three stages
+* :func:`fa_bwd_delta`, :func:`fa_bwd_dkdv`, :func:`fa_bwd_dq` -- fa_bwd's stages,
+  separately (for bf16 the dQ stage also writes delta)
 * :func:`fa_bwd_workspace_size`, :func:`fa_status_string`
 * :func:`fa_measure_mfma_rate` -- a measurement aid: the matrix-core rate on
   realistic operand bits, against which the kernels' rates are also read
