@@ -161,6 +161,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // Query rows past N get LSE = +inf and delta = 0, so their P and dS are
   // exactly zero and no bounds test is needed on the query side.  Key columns
   // past N (K, V rows zero) only reach dK/dV columns that are never written.
+  // delta is stored negated: it is the starting value of the dP accumulators,
+  // which then hold dP - delta with no vector op.
   auto store_stats = [&](int it, int buf) {
     const int q = it * BM + (tid & (BM - 1));
     // (with a bias, an LSE of -inf -- a row with no finite score -- becomes
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const bool live = q < N && (!BIAS || sreg != -__builtin_inff());
     if (tid < 2 * BM)
       lst[buf][tid / BM][tid & (BM - 1)] =
-          tid < BM ? (live ? sreg * kLog2e : __builtin_inff()) : (q < N ? sreg : 0.f);
+          tid < BM ? (live ? sreg * kLog2e : __builtin_inff()) : (q < N ? -sreg : 0.f);
   };
 
   f32x16 adk[NCB], adv[NCB];
@@ -199,6 +201,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const uint16_t* Ot = otile(bufc);
     const int qbase = it * BM;
     constexpr int NA = 2 * NT, NB = 4 * NCB, DEPTH = 4;
+    // LSE*log2e and -delta of the 16 rows a lane sees in half qb, read once
+    // (-delta in C-layout order, as the starting value of dP)
+    f32x4 l2v[4];
+    f32x16 ndl_init;
     // operand fetches
     auto fetch_a = [&](int qb, int k) -> bf16x8 {  // k-th product of G_A(qb)
       const uint16_t* base = (k & 1) ? Ot : Qt;
@@ -212,7 +218,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     auto op_a = [&](int qb, int k, const bf16x8& a) {
       if (k < 2) {
         if (k == 0) s[qb] = mfma_bf16(a, kf[0], f32x16{});
-        else dp[qb] = mfma_bf16(a, vf[0], f32x16{});
+        else dp[qb] = mfma_bf16(a, vf[0], ndl_init);
       } else if (k & 1) {
         dp[qb] = mfma_bf16(a, vf[k >> 1], dp[qb]);
       } else {
@@ -224,18 +230,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       if (k & 1) adk[cb] = mfma_bf16(a, db[qb][h], adk[cb]);
       else adv[cb] = mfma_bf16(a, pb[qb][h], adv[cb]);
     };
-    // LSE*log2e and delta of the 16 rows a lane sees in half qb, read once
-    f32x4 l2v[4], dlv[4];
-    auto load_half_stats = [&](int qb) {
+    auto load_half_lse = [&](int qb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        l2v[q4] = *reinterpret_cast<const f32x4*>(&lst[BUF][0][32 * qb + 8 * q4 + 4 * g]);
+    };
+    auto load_half_ndelta = [&](int qb) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        l2v[q4] = *reinterpret_cast<const f32x4*>(&lst[BUF][0][32 * qb + 8 * q4 + 4 * g]);
-        dlv[q4] = *reinterpret_cast<const f32x4*>(&lst[BUF][1][32 * qb + 8 * q4 + 4 * g]);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&lst[BUF][1][32 * qb + 8 * q4 + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ndl_init[4 * q4 + e] = v[e];
       }
     };
     // softmax-backward arithmetic of element i (0..15) of half qb
     auto soft_elem = [&](int qb, int i) {
-      const float l2 = l2v[i >> 2][i & 3], dl = dlv[i >> 2][i & 3];
+      const float l2 = l2v[i >> 2][i & 3];
       float arg = -l2;
       if constexpr (BIAS) arg = fmaf(bsv[BUF][qb][i], kLog2e, arg);
       float p = exp2_fast(fmaf(s[qb][i], scale_log2, arg));
@@ -243,7 +253,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
         if (kcol - (qbase + 32 * qb + 4 * g) > 8 * (i >> 2) + (i & 3)) p = 0.f;
       }
       s[qb][i] = p;
-      dp[qb][i] = p * (dp[qb][i] - dl);
+      dp[qb][i] = p * dp[qb][i];  // dP - delta from the accumulator
       if ((i & 7) == 7) {
         pb[qb][i >> 3] = to_bf16x8(s[qb], i - 7);
         db[qb][i >> 3] = to_bf16x8(dp[qb], i - 7);
@@ -276,15 +286,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     auto stage_at = [&](int op) {
       if (op % SEV == 0) stage_one(qr, orr, std::integral_constant<int, BUF ^ 1>{}, op / SEV);
     };
-    load_half_stats(0);
+    load_half_lse(0);
+    load_half_ndelta(0);
     stream(false, 0, NA, [&](int k) { stage_at(k); });
+    load_half_ndelta(1);
     // the 16 softmax elements of a half are spread evenly over a stream
     stream(false, 1, NA, [&](int k) {
 #pragma unroll
       for (int i = k * 16 / NA; i < (k + 1) * 16 / NA; ++i) soft_elem(0, i);
       stage_at(NA + k);
     });
-    load_half_stats(1);
+    load_half_lse(1);
     stream(true, 0, NB, [&](int k) {
 #pragma unroll
       for (int i = k * 16 / NB; i < (k + 1) * 16 / NB; ++i) soft_elem(1, i);
