@@ -102,6 +102,17 @@ def test_bf16_dense_bias(N, d, causal):
                f"bf16 dense bias 2x3x{N}x{d} causal={causal}")
 
 
+@pytest.mark.parametrize("N", [31, 32, 33, 63, 64, 96, 97, 129])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_bias_tile_boundaries(N, causal):
+    """Sequence lengths at and around the key-tile widths of the bias kernels
+    (32-key tiles in the d = 128 forward, 64-key tiles elsewhere)."""
+    d = 128
+    inp = fa_inputs.make_inputs((1, 2, N, d), "bf16", seed=7 * N + int(causal))
+    check_case(inp, dense_bias(1, 2, N, seed=11 * N), 1 / math.sqrt(d), causal,
+               f"bf16 dense bias 1x2x{N}x{d} causal={causal}")
+
+
 @pytest.mark.parametrize("N", [65, 1000])
 @pytest.mark.parametrize("kind", ["shared", "keypad", "window"])
 @pytest.mark.parametrize("causal", [False, True])
