@@ -406,6 +406,8 @@ def main():
                          "wall time has passed, so that the shader clock has settled")
     ap.add_argument("--workload", default=MAIN)
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
+    ap.add_argument("--rate-probe", action="store_true",
+                    help="time the matrix-core rate probe also with --no-extra")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads the CPU oracle runs (0: all B*H heads of the workload)")
@@ -488,7 +490,7 @@ def main():
             log(f"{name}: {r}")
 
     measured = None
-    if not args.no_extra:
+    if not args.no_extra or args.rate_probe:
         measured = measure_mfma_rates()
         log(f"measured matrix-core rates (TFLOP/s): {measured}")
         roof["measured_peak"] = measured[w.dtype] if w.dtype in measured else None

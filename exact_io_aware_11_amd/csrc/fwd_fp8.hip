@@ -48,12 +48,19 @@ namespace fa {
 namespace {
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-// 16-byte-chunk XOR swizzle of a [64 keys][D bytes] tile: conflict-free for
-// the 16-byte row reads (16 consecutive rows, one chunk) and for the
-// transposing 8-byte reads (8 consecutive rows, one chunk).
+// 16-byte-chunk XOR swizzle of a [64 keys][D bytes] tile.  LDS serves a
+// 16-byte read 16 lanes at a time and an 8-byte read 32 lanes at a time, 256
+// bytes (64 four-byte banks, 256 / D tile rows) per pass.  The K reads of one
+// pass cover 16 rows of the form {0..3, 4..7, 16..19, 20..23} (+8) at one
+// chunk, the transposing V reads 8 consecutive rows at two adjacent chunks;
+// the XOR value (bits of the row: 2, 1 and 4 at D = 128; 2 and 4 at D = 64)
+// differs over the rows of a pass that share banks, so both are
+// conflict-free.  It repeats every 32 rows: the second 32-key block of a
+// tile reuses the first one's offsets.
 template <int D>
 __device__ __forceinline__ int sw8(int row) {
-  return (row / (256 / D)) & (D / 16 - 1);
+  if constexpr (D == 128) return (((row >> 1) & 3) << 1) | ((row >> 4) & 1);
+  else return (((row >> 2) & 1) << 1) | ((row >> 4) & 1);
 }
 template <int D>
 __device__ __forceinline__ int tile_byte(int row, int chunk) {
