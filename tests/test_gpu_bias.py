@@ -204,3 +204,30 @@ def test_full_bf16_causal_bias_fwd_b2h32n8192d128():
         dead = check_lse(f"{tag} LSE rows", lse64[b, h, rows], lse_ref, "bf16")
         assert np.all(o64[b, h, rows][dead] == 0.0)
         check(f"{tag} O rows", o64[b, h, rows], o_ref, "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_longest_sequence_keypad_bias(d, causal):
+    """N = 2^17 in one head with a key-padding bias [1,1,1,N] (keys past a
+    drawn length masked): the bias kernels' long-sequence offsets and tile
+    counts (32-key tiles at d = 128), sampled rows against the oracle,
+    including rows past the padding length and the last rows."""
+    N = 1 << 17
+    inp = fa_inputs.make_inputs((1, 1, N, d), "bf16", seed=d + int(causal), with_dout=False)
+    b_np = fa_inputs.draw_bias((1, 1), N, seed=5 + d, kind="keypad")
+    dev = tuple(to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    bias_dev, _ = bias_views(b_np, N)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_fwd_bias(dev, bias_dev, scale, causal, "bf16")
+    o64, lse64 = to_f64(o), to_f64(lse)
+    rows = np.unique(np.concatenate([np.random.default_rng(d).choice(N, 12, replace=False),
+                                     [0, 31, 32, 33, 4095, N - 33, N - 2, N - 1]]))
+    qs, ks, vs = (exact_values(x[0, 0], "bf16") for x in (inp.q, inp.k, inp.v))
+    o_ref, lse_ref = oracle.attn_fwd_rows(qs, ks, vs, rows, scale, causal,
+                                          bias_rows=b_np[0, 0, 0, :N].astype(np.float64))
+    tag = f"keypad bias 1x1x{N}x{d} causal={causal}"
+    say(f"{tag}: {int(np.isneginf(lse_ref).sum())} of {rows.size} sampled rows empty")
+    dead = check_lse(f"{tag} LSE rows", lse64[0, 0, rows], lse_ref, "bf16")
+    assert np.all(o64[0, 0, rows][dead] == 0.0)
+    check(f"{tag} O rows", o64[0, 0, rows], o_ref, "bf16")
