@@ -543,9 +543,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     };
     auto soft_elem = [&](int b, int i) {  // key of element i: key0 + 32 b + 8 (i / 4) + 4 g + i % 4
       float p = exp2_fast(fmaf(s[b][i], scale_log2, -lse2));
-      if constexpr (masked) {
+      if constexpr (masked && BIAS) {
         const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3);
-        if ((CAUSAL && key > qrow) || (BIAS && key >= N)) p = 0.f;
+        if ((CAUSAL && key > qrow) || key >= N) p = 0.f;
+      } else if constexpr (masked) {  // causal only: the lane index is recomputed here, so no
+        // register is held across the whole scan for the mask (a spill and a full memory wait
+        // in the diagonal tiles otherwise)
+        const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * (ln >> 5) + (i & 3);
+        if (key > q0 + (ln & 31)) p = 0.f;
       }
       dp[b][i] = p * (dp[b][i] - del);
       if ((i & 7) == 7) db[b][i >> 3] = to_bf16x8(dp[b], i - 7);
