@@ -8,10 +8,10 @@
 // end.  Scores and probabilities live only in registers.
 //
 // Work split (explainer V2 section; FA1 page section 10.2.5): a workgroup of
-// 4 waves handles a (batch, head, block of 128 query rows) -- under the causal
-// mask two blocks, u and n-1-u, one after the other, so that every workgroup
-// visits the same number of key tiles; each wave owns 32 query rows and scans
-// every visible key tile of 64 keys (32 with a bias at d = 128).
+// 4 or 8 waves handles a (batch, head, block of 128 or 256 query rows) --
+// under the causal mask two blocks, u and n-1-u, one after the other, so that
+// every workgroup visits the same number of key tiles; each wave owns 32 query
+// rows and scans every visible key tile of 64 keys (32 with a bias at d = 128).
 //
 // gfx950 mapping:
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K (A operand) comes from LDS,
@@ -42,9 +42,10 @@
 
 namespace fa {
 
-// Two workgroups per CU (64 KiB of LDS and at most 256 registers per wave); at
-// d = 64 without a bias three (32 KiB of LDS each; the kernel fits in a third
-// of the register file with a prefetch depth of 3).  A bias at d = 128 takes
+// Two waves per SIMD (64 KiB of LDS per workgroup and at most 256 registers
+// per wave: two workgroups of 4 waves or one of 8 per CU); at d = 64 without
+// a bias three workgroups of 4 (32 KiB of LDS each; the kernel fits in a
+// third of the register file with a prefetch depth of 3).  A bias at d = 128 takes
 // 32-key tiles: two 64-key score tiles and a tile's bias do not fit in the
 // registers of two workgroups per CU, one 32-key score tile less does.
 template <int D, bool CAUSAL, int WAVES, bool BIAS>
@@ -482,9 +483,6 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   }
 }
 
-#ifndef FA_FWD_WAVES
-#define FA_FWD_WAVES 4
-#endif
 template <int D, bool CAUSAL, int WAVES, bool BIAS>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   constexpr int BM = 32 * WAVES;
@@ -498,11 +496,14 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   return hipGetLastError();
 }
 
+// Waves per workgroup: at d = 128 eight (256 query rows, one workgroup per CU,
+// still two waves per SIMD), so each K/V tile staged into LDS serves twice
+// the rows; at d = 64 four (three workgroups, twelve waves, per CU), and four
+// with a bias (both measured faster that way).
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_b(const FwdArgs& a) {
-  constexpr int W = FA_FWD_WAVES;
-  return a.bias.p ? launch_fwd_bf16_t<D, CAUSAL, W, true>(a)
-                  : launch_fwd_bf16_t<D, CAUSAL, W, false>(a);
+  return a.bias.p ? launch_fwd_bf16_t<D, CAUSAL, 4, true>(a)
+                  : launch_fwd_bf16_t<D, CAUSAL, D == 128 ? 8 : 4, false>(a);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {

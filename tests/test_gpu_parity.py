@@ -71,7 +71,7 @@ def test_fp32_shapes(B, H, N, d, causal):
 # --------------------------------------------------------------------------- #
 # bf16 small shapes: several tiles, ragged tails, both masks, both head sizes
 # --------------------------------------------------------------------------- #
-@pytest.mark.parametrize("N", [1, 65, 257, 1000])
+@pytest.mark.parametrize("N", [1, 65, 257, 600, 1000])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_fwd_bwd_small(N, d, causal):
