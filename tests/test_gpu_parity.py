@@ -79,11 +79,11 @@ def test_bf16_fwd_bwd_small(N, d, causal):
     full_check_bwd(inp, 1 / math.sqrt(d), causal, f"bf16 2x3x{N}x{d}")
 
 
-@pytest.mark.parametrize("N", [63, 64, 127, 128, 129, 191, 192])
+@pytest.mark.parametrize("N", [63, 64, 127, 128, 129, 191, 192, 255, 256, 513])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_tile_boundaries(N, d, causal):
-    """Lengths at and around the 64-key tile and the 128-row block."""
+    """Lengths at and around the 64-key tile and the 128- and 256-row blocks."""
     inp = fa_inputs.make_inputs((1, 2, N, d), "bf16", seed=13 * N + d + int(causal))
     full_check_bwd(inp, 1 / math.sqrt(d), causal, f"bf16 1x2x{N}x{d}")
 
