@@ -46,7 +46,7 @@ def values(mx):
             oracle.decode_mx_e4m3fn(mx.v, mx.vs, -2))
 
 
-@pytest.mark.parametrize("N", [1, 100, 513, 1000])
+@pytest.mark.parametrize("N", [1, 31, 32, 33, 64, 65, 100, 128, 129, 513, 1000])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_mxfp8_fwd_small(N, d, causal):

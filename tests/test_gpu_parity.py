@@ -88,7 +88,7 @@ def test_bf16_tile_boundaries(N, d, causal):
     full_check_bwd(inp, 1 / math.sqrt(d), causal, f"bf16 1x2x{N}x{d}")
 
 
-@pytest.mark.parametrize("N", [1, 100, 513, 1000])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 100, 127, 128, 129, 513, 1000])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_fwd_small(N, d, causal):
