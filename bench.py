@@ -417,7 +417,7 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: every (batch, head) is independent, so "
               "several GPUs would each run this same kernel on their share of heads; "
-              "multi-GPU runs are not part of this build.", file=sys.stderr)
+              "there is no multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
 
     import torch
