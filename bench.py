@@ -216,6 +216,36 @@ def time_calls(fn, reps, warmup, warm_s=0.0):
     return sum(ms) / len(ms), ms[len(ms) // 2]
 
 
+def time_delta(w, reps, warmup, warm_s=0.0):
+    """The standalone delta kernel (fa_bwd_delta: delta_i = dO_i . O_i, HBM-bound) on the
+    workload's shape; the bf16 backward forms delta inside its dQ kernel instead.  Thirty
+    back-to-back calls between two events, cycling over six (O, dO) pairs -- 384 MiB at the
+    default shape, more than the 256 MB last-level cache -- so that every call reads HBM and
+    the event overhead is spread; returns the mean and median time per call."""
+    import torch
+
+    import exact_io_aware_11_amd as fa
+
+    B, H, N, d = w.shape
+    g = torch.Generator(device="cuda").manual_seed(7)
+    pairs = [tuple(torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+                   for _ in range(2)) for _ in range(6)]
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device="cuda")
+    calls = 30
+
+    def run():
+        for i in range(calls):
+            o, do = pairs[i % len(pairs)]
+            # (q, k, v and the gradients are neither read nor written by this stage)
+            fa.fa_bwd_delta(o, o, o, o, do, lse, o, o, o, ws, w.scale, w.causal)
+
+    mean, med = time_calls(run, reps, warmup, warm_s)
+    del pairs, lse, ws
+    torch.cuda.empty_cache()
+    return mean / calls, med / calls
+
+
 def time_fwd_only(w, reps, warmup, warm_s=0.0):
     import torch
 
@@ -459,6 +489,7 @@ def main():
 
     extra = {}
     bias_lines = {}
+    hbm_lines = {}
     if not args.no_extra:
         for name in EXTRA:
             if name == w.name:
@@ -488,6 +519,18 @@ def main():
                           warmup=3, warm_s=min(args.warm_seconds, 1.0))
             bias_lines[name] = r
             log(f"{name}: {r}")
+        if w.backward and w.dtype == "bf16":  # (for fp32 the delta kernel is a stage of the step)
+            mean, med = time_delta(w, reps=max(10, args.steps // 2), warmup=3,
+                                   warm_s=min(args.warm_seconds, 1.0))
+            gbs = work["delta_bytes"] / (mean * 1e-3) / 1e9
+            hbm_lines["delta"] = {"ms": round(mean, 4), "ms_median": round(med, 4),
+                                  "GB/s": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                  "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                                  "bytes": work["delta_bytes"],
+                                  "note": "fa_bwd_delta on this workload's shape (reads O and dO, "
+                                          "writes delta; the bf16 fa_bwd forms delta in dQ): 30 "
+                                          "back-to-back calls over 6 buffer pairs, per call"}
+            log(f"delta kernel: {hbm_lines['delta']}")
 
     measured = None
     if not args.no_extra or args.rate_probe:
@@ -522,6 +565,7 @@ def main():
         "roofline": roof,
         "forward_workloads": extra,
         "bias_workloads": bias_lines,
+        "hbm_kernels": hbm_lines,
         "mfma_rate_measured": None if measured is None else dict(
             measured, unit="TFLOP/s",
             note="pure 32x32 matrix-core products on pseudo-random operands, every CU, warm "

@@ -253,54 +253,83 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
 }
 
 // delta_i = sum_c dO_ic O_ic (FA1 page, section 10.2.4), float32 result.
-// 16 lanes per row, 16 rows per workgroup, 16-byte loads.
+// HBM-bound: a row takes LPR lanes (one 16-byte chunk of O and of dO per
+// lane and pass, PER passes), and every lane works on R rows of its
+// workgroup, issuing all its loads before any arithmetic so that enough
+// bytes are in flight per CU to keep HBM busy.
+template <bool BF16, int D>
+struct DeltaShape {
+  static constexpr int CH = BF16 ? D / 8 : D / 4;     // 16-byte chunks per row
+  static constexpr int LPR = CH < 16 ? CH : 16;       // lanes per row
+  static constexpr int PER = CH / LPR;                // chunks per lane and row
+  static constexpr int R = 4;                         // rows per lane
+  static constexpr int ROWS = R * 256 / LPR;          // rows per workgroup
+};
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void delta_kernel(const void* __restrict__ Ov,
                                                     const void* __restrict__ dOv,
                                                     float* __restrict__ delta, long rows) {
-  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  float acc = 0.f;
-  if (row < rows) {
-    if constexpr (BF16) {
-      constexpr int CH = D / 8;
-      const uint4* o = reinterpret_cast<const uint4*>((const uint16_t*)Ov + row * D);
-      const uint4* g = reinterpret_cast<const uint4*>((const uint16_t*)dOv + row * D);
-      for (int c = sub; c < CH; c += 16) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, o[c]);
-        const bf16x8 b = __builtin_bit_cast(bf16x8, g[c]);
+  using S = DeltaShape<BF16, D>;
+  constexpr int LPR = S::LPR, PER = S::PER, R = S::R, CH = S::CH;
+  const int sub = threadIdx.x % LPR;
+  const long row0 = (long)blockIdx.x * S::ROWS + threadIdx.x / LPR;  // rows row0 + (256 / LPR) r
+  const uint4* o = reinterpret_cast<const uint4*>(Ov);
+  const uint4* g = reinterpret_cast<const uint4*>(dOv);
+  uint4 a[R][PER], b[R][PER];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
-      }
-    } else {
-      constexpr int CH = D / 4;
-      const float4* o = reinterpret_cast<const float4*>((const float*)Ov + row * D);
-      const float4* g = reinterpret_cast<const float4*>((const float*)dOv + row * D);
-      for (int c = sub; c < CH; c += 16) {
-        const float4 a = o[c], b = g[c];
-        acc = fmaf(a.x, b.x, acc);
-        acc = fmaf(a.y, b.y, acc);
-        acc = fmaf(a.z, b.z, acc);
-        acc = fmaf(a.w, b.w, acc);
+  for (int r = 0; r < R; ++r) {
+    const long row = row0 + (long)(256 / LPR) * r;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      if (row < rows) {
+        a[r][c] = o[row * CH + sub + LPR * c];
+        b[r][c] = g[row * CH + sub + LPR * c];
+      } else {
+        a[r][c] = b[r][c] = uint4{0u, 0u, 0u, 0u};
       }
     }
   }
-  acc += __shfl_xor(acc, 8, 16);
-  acc += __shfl_xor(acc, 4, 16);
-  acc += __shfl_xor(acc, 2, 16);
-  acc += __shfl_xor(acc, 1, 16);
-  if (row < rows && sub == 0) delta[row] = acc;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      if constexpr (BF16) {
+        const bf16x8 x = __builtin_bit_cast(bf16x8, a[r][c]);
+        const bf16x8 y = __builtin_bit_cast(bf16x8, b[r][c]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+      } else {
+        const float4 x = __builtin_bit_cast(float4, a[r][c]);
+        const float4 y = __builtin_bit_cast(float4, b[r][c]);
+        acc = fmaf(x.x, y.x, acc);
+        acc = fmaf(x.y, y.y, acc);
+        acc = fmaf(x.z, y.z, acc);
+        acc = fmaf(x.w, y.w, acc);
+      }
+    }
+#pragma unroll
+    for (int m = LPR / 2; m > 0; m /= 2) acc += __shfl_xor(acc, m, LPR);
+    const long row = row0 + (long)(256 / LPR) * r;
+    if (row < rows && sub == 0) delta[row] = acc;
+  }
+}
+
+template <bool BF16, int D>
+static void launch_delta_t(const BwdArgs& a, long rows) {
+  constexpr int ROWS = DeltaShape<BF16, D>::ROWS;
+  const dim3 grid((unsigned)((rows + ROWS - 1) / ROWS));
+  hipLaunchKernelGGL((delta_kernel<BF16, D>), grid, dim3(256), 0, a.stream, a.o, a.dout, a.delta, rows);
 }
 
 hipError_t launch_delta(const BwdArgs& a, bool bf16) {
   const long rows = a.BH * (long)a.N;
-  const dim3 grid((unsigned)((rows + 15) / 16));
   if (bf16) {
-    if (a.d == 64) hipLaunchKernelGGL((delta_kernel<true, 64>), grid, dim3(256), 0, a.stream, a.o, a.dout, a.delta, rows);
-    else hipLaunchKernelGGL((delta_kernel<true, 128>), grid, dim3(256), 0, a.stream, a.o, a.dout, a.delta, rows);
+    if (a.d == 64) launch_delta_t<true, 64>(a, rows);
+    else launch_delta_t<true, 128>(a, rows);
   } else {
-    if (a.d == 64) hipLaunchKernelGGL((delta_kernel<false, 64>), grid, dim3(256), 0, a.stream, a.o, a.dout, a.delta, rows);
-    else hipLaunchKernelGGL((delta_kernel<false, 128>), grid, dim3(256), 0, a.stream, a.o, a.dout, a.delta, rows);
+    if (a.d == 64) launch_delta_t<false, 64>(a, rows);
+    else launch_delta_t<false, 128>(a, rows);
   }
   return hipGetLastError();
 }
