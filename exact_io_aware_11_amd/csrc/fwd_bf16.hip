@@ -424,9 +424,23 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     l_run += lsum[0] + lsum[1];
     guard(fmaxf(mxp[0], mxp[1]));
   };
-  // Last tile: no next scores; P_j then O^T += V_j^T P_j^T.
-  auto step_last = [&](auto parity) __attribute__((always_inline)) {
+  // This wave's last tile j: no next scores; P_j then O^T += V_j^T P_j^T.
+  // Under the causal mask a wave's last tile can come before the workgroup's
+  // (n_use below); the wave then still stages its share of K_{j+2}, V_{j+1}.
+  auto stage_next = [&](auto parity, int j) __attribute__((always_inline)) {
+    using PN = std::integral_constant<int, decltype(parity)::value ^ 1>;
+    const auto kres = tile_rsrc(Kh, (j + 2) * BN);
+    const auto vres = tile_rsrc(Vh, (j + 1) * BN);
+#pragma unroll
+    for (int L = 0; L < 2 * LPW; ++L) {
+      const int x = L % LPW;
+      if (L >= LPW) load_lds16(vres, vtile(PN{}) + (wave * LPW + x) * 512, ldoff[x]);
+      else load_lds16(kres, ktile(parity) + (wave * LPW + x) * 512, ldoff[x]);
+    }
+  };
+  auto step_last = [&](auto parity, int j) __attribute__((always_inline)) {
     barrier_vm<0>();
+    if (j + 1 < n_tiles) stage_next(parity, j);  // (causal: tiles past this wave's queries follow)
     bf16x8 p[2 * NH];
     exps(sc_of(parity), p);
     pv(vtile(parity), p);
@@ -435,20 +449,37 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   // scores is correct for any tile, just slower), then the last tile.
   using NOMASK = std::false_type;
   using MASK = std::true_type;
+  // Causal without a bias: this wave's tiles end at n_use, the last one with
+  // a key at or before its last query; the workgroup's diagonal tiles past
+  // it would give all-zero P and all-masked scores.  The wave stops its
+  // products there, and for the rest of the workgroup's tiles only stages its
+  // share and meets the barriers (its SIMD partner has the matrix core to
+  // itself meanwhile).  j_full < n_use always: the block's first row sees
+  // every key before the block.
+  const int n_use = CAUSAL && !BIAS ? min(n_tiles, (q0 + 31) / BN + 1) : n_tiles;
   int j = 0;
   for (; j + 2 < j_full; j += 2) {
     step(B0{}, NOMASK{}, j);
     step(B1{}, NOMASK{}, j + 1);
   }
-  for (; j + 2 < n_tiles; j += 2) {
+  for (; j + 2 < n_use; j += 2) {
     step(B0{}, MASK{}, j);
     step(B1{}, MASK{}, j + 1);
   }
-  if (j + 1 < n_tiles) {  // two tiles left
+  if (j + 1 < n_use) {  // two tiles left
     step(B0{}, MASK{}, j);
-    step_last(B1{});
+    step_last(B1{}, ++j);
   } else {
-    step_last(B0{});
+    step_last(B0{}, j);
+  }
+  if constexpr (CAUSAL && !BIAS) {
+    for (++j; j < n_tiles; ++j) {  // tiles past this wave's queries
+      barrier_vm<0>();
+      if (j + 1 < n_tiles) {
+        if (j & 1) stage_next(B1{}, j);
+        else stage_next(B0{}, j);
+      }
+    }
   }
   wait_vm<0>();  // no direct load may still be landing when the workgroup ends
 
