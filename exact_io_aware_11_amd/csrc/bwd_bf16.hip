@@ -628,9 +628,34 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     step(B0{}, std::false_type{}, j);
     step(B1{}, std::false_type{}, j + 1);
   }
-  for (; j < n_tiles; j += 2) {  // the causal diagonal tiles (masking any tile is correct)
-    step(B0{}, std::true_type{}, j);
-    if (j + 1 < n_tiles) step(B1{}, std::true_type{}, j + 1);
+  if constexpr (CAUSAL && !BIAS) {
+    // This wave's tiles end at n_use, the last one holding a key at or
+    // before its last query (j_full < n_use: the block's first query sees
+    // every earlier key).  For the workgroup's remaining diagonal tile the
+    // wave only stages its share of the next tile and meets the barrier.
+    const int n_use = min(n_tiles, (q0 + 31) / BN + 1);
+    for (; j + 1 < n_use; j += 2) {
+      step(B0{}, std::true_type{}, j);
+      step(B1{}, std::true_type{}, j + 1);
+    }
+    if (j < n_use) step(B0{}, std::true_type{}, j++);
+    auto idle = [&](auto bufc, int jj) {
+      barrier_vm<0>();
+      const auto kr = tile_rsrc(Kh, (jj + 1) * BN);
+      const auto vr = tile_rsrc(Vh, (jj + 1) * BN);
+#pragma unroll
+      for (int L = 0; L < 2 * LPW; ++L)
+        stage_one(kr, vr, std::integral_constant<int, decltype(bufc)::value ^ 1>{}, L);
+    };
+    for (; j < n_tiles; ++j) {
+      if (j & 1) idle(B1{}, j);
+      else idle(B0{}, j);
+    }
+  } else {
+    for (; j < n_tiles; j += 2) {  // the causal diagonal tiles (masking any tile is correct)
+      step(B0{}, std::true_type{}, j);
+      if (j + 1 < n_tiles) step(B1{}, std::true_type{}, j + 1);
+    }
   }
   wait_vm<0>();  // the last (unused) loads land before the workgroup's LDS is released
 
