@@ -311,6 +311,11 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   constexpr int DEPTH = D == 64 ? 3 : 4;
   constexpr int NS = NH * (D / 16), NOPS = NS + 2 * NH * (D / 32);  // S products come first
   constexpr int EXP_OPS = NH == 2 ? NS + 2 * (D / 32) : NS + 2, MAX_OPS = NH == 2 ? 12 : 4;
+  // the last element of key chunk kc (element 8 kc + 7 of half kc / 2) gets its phase (c), which
+  // packs the chunk, in product slot (its phase-(a) slot) + 2, before the chunk's first PV product
+  static_assert((7 * EXP_OPS) / (16 * NH) + 2 < NS, "chunk 0 packed before its first PV product");
+  static_assert(((16 * NH - 1) * EXP_OPS) / (16 * NH) + 2 < NS + (2 * NH - 1) * (D / 32),
+                "last chunk packed before its first PV product");
   auto step = [&](auto parity, auto maskc, int j) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;  // j % 2
     constexpr bool MASK_NEXT = decltype(maskc)::value;
