@@ -1,21 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-A step is one pass of the whole path over one batch of synthetic input: the
-forward (fa_fwd) and the backward stages (fa_bwd_dq, which also forms delta,
-then fa_bwd_dkdv -- exactly what fa_bwd enqueues for bf16), on the bf16 causal workload
-B=2, H=16, N=4096, d=128 unless --workload says otherwise.  Inputs are resident
-in device memory before the timed region starts.  Each kernel is bracketed by
-HIP events on the stream it runs on, so per-kernel durations are measured live.
+A step is one pass of the workload's whole path over one batch of synthetic
+input.  The default workload is the bf16 causal forward at B=2, H=32, N=8192,
+d=128 (one fa_fwd per step); with --workload a fwd+bwd workload steps through
+the forward and the backward stages (fa_bwd_dq, which also forms delta, then
+fa_bwd_dkdv -- exactly what fa_bwd enqueues for bf16).  Inputs are resident in
+device memory before the timed region starts.  Each kernel is bracketed by HIP
+events on the stream it runs on, so per-kernel durations are measured live.
 
-After the timed steps the forward-only workloads (bf16 causal N=8192 d=128,
-bf16 N=2048 d=64, fp8 N=16384 d=128 with per-tensor scales and with e8m0
-block scales) and two runs with an additive bias on the scores (the N=8192
-forward with a dense bias, the default workload's forward and backward with a
-sliding-window bias) are timed the same way and reported in the same JSON
-line, as is the launch-bound float32 workload (N=128, in microseconds), and
-the CPU oracle is timed on a bounded sample of the main workload on this
-host's cores.
+After the timed steps the other workloads are timed the same way and reported
+in the same JSON line: the bf16 causal forward+backward at B=2, H=16, N=4096,
+d=128 (per-kernel times and fractions of peak), the forward-only workloads
+(bf16 N=2048 d=64, fp8 N=16384 d=128 with per-tensor scales and with e8m0
+block scales), two runs with an additive bias on the scores (the N=8192
+forward with a dense bias, the N=4096 forward and backward with a
+sliding-window bias), the launch-bound float32 workload (N=128, in
+microseconds), the HBM-bound delta kernel, and the CPU oracle on a bounded
+sample of the main workload on this host's cores.
 
 Prints ONE JSON line.  Only N=1 GPU is supported (--gpus > 1 exits).
 """
@@ -35,7 +37,8 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "fp32": 157.3}  # dense, 256 CU x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOPS (bf16, fp8) and % of MI355X MFMA peak"
-MAIN = "bf16_causal_fwdbwd_b2h16n4096d128"
+MAIN = "bf16_causal_fwd_b2h32n8192d128"
+FWDBWD_EXTRA = "bf16_causal_fwdbwd_b2h16n4096d128"
 EXTRA = ["bf16_causal_fwd_b2h32n8192d128", "bf16_fwd_b4h16n2048d64", "fp8_fwd_b1h32n16384d128"]
 MX_EXTRA = ("mxfp8_fwd_b1h32n16384d128", (1, 32, 16384, 128))
 # Additive bias on the scores (one [N, N] float32 bias shared by every batch
@@ -426,6 +429,34 @@ def calibrate_copy(nbytes: int = 1 << 30, reps: int = 3):
           flush=True)
 
 
+def step_report(w, ms, per):
+    """Whole-step TFLOP/s, per-kernel figures and the roofline of the dominant
+    kernel (the one with the largest share of the step) for one timed workload."""
+    work = algorithmic_work(w)
+    total_flops = work["fwd"] + (work["dkdv"] + work["dq"] if w.backward else 0.0)
+    peak = PEAK_TFLOPS[w.dtype]
+    kernels = {}
+    for s, t in per.items():
+        if s == "delta":
+            gbs = work["delta_bytes"] / (t * 1e-3) / 1e9
+            kernels[s] = {"ms": round(t, 4), "GB/s": round(gbs, 1),
+                          "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        else:
+            tf = work[s] / (t * 1e-3) / 1e12
+            kernels[s] = {"ms": round(t, 4), "TFLOP/s": round(tf, 1), "frac": round(tf / peak, 4)}
+    dom = max(per, key=per.get)
+    if dom == "delta":
+        ach = work["delta_bytes"] / (per[dom] * 1e-3) / 1e9
+        roof = {"kernel": "delta", "bound": "hbm", "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    else:
+        ach = work[dom] / (per[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
+    roof["traffic"] = measured_traffic(w.name, dom)
+    return total_flops / (ms * 1e-3) / 1e12, kernels, roof
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -462,30 +493,20 @@ def main():
     w = fa_inputs.WORKLOADS[args.workload]
     log(f"workload {w.name} steps={args.steps} warmup={args.warmup}")
     ms, wall, per = time_main(w, args.steps, args.warmup, args.warm_seconds)
-    work = algorithmic_work(w)
-    total_flops = work["fwd"] + (work["dkdv"] + work["dq"] if w.backward else 0.0)
+    value, kernels, roof = step_report(w, ms, per)
     peak = PEAK_TFLOPS[w.dtype]
-    kernels = {}
-    for s, t in per.items():
-        if s == "delta":
-            gbs = work["delta_bytes"] / (t * 1e-3) / 1e9
-            kernels[s] = {"ms": round(t, 4), "GB/s": round(gbs, 1),
-                          "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
-        else:
-            tf = work[s] / (t * 1e-3) / 1e12
-            kernels[s] = {"ms": round(t, 4), "TFLOP/s": round(tf, 1), "frac": round(tf / peak, 4)}
-    dom = max(per, key=per.get)
-    if dom == "delta":
-        ach = work["delta_bytes"] / (per[dom] * 1e-3) / 1e9
-        roof = {"kernel": "delta", "bound": "hbm", "achieved": round(ach, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
-    else:
-        ach = work[dom] / (per[dom] * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
-    roof["traffic"] = measured_traffic(w.name, dom)
-    value = total_flops / (ms * 1e-3) / 1e12
     log(f"step {ms:.3f} ms  {value:.1f} TFLOP/s  kernels {kernels}")
+
+    fwdbwd = {}
+    if not args.no_extra and w.name != FWDBWD_EXTRA:
+        x = fa_inputs.WORKLOADS[FWDBWD_EXTRA]
+        x_ms, _, x_per = time_main(x, args.steps, min(args.warmup, 3),
+                                   min(args.warm_seconds, 1.0))
+        x_value, x_kernels, x_roof = step_report(x, x_ms, x_per)
+        fwdbwd[x.name] = {"ms_per_step": round(x_ms, 4), "TFLOP/s": round(x_value, 1),
+                          "frac_of_peak": round(x_value / PEAK_TFLOPS[x.dtype], 4),
+                          "passes": "fwd+bwd", "kernels": x_kernels, "roofline": x_roof}
+        log(f"{x.name}: step {x_ms:.3f} ms {x_value:.1f} TFLOP/s kernels {x_kernels}")
 
     extra = {}
     bias_lines = {}
@@ -519,15 +540,18 @@ def main():
                           warmup=3, warm_s=min(args.warm_seconds, 1.0))
             bias_lines[name] = r
             log(f"{name}: {r}")
-        if w.backward and w.dtype == "bf16":  # (for fp32 the delta kernel is a stage of the step)
-            mean, med = time_delta(w, reps=max(10, args.steps // 2), warmup=3,
+        xd = w if w.backward else fa_inputs.WORKLOADS[FWDBWD_EXTRA]
+        if xd.dtype == "bf16":  # (for fp32 the delta kernel is a stage of the step)
+            work = algorithmic_work(xd)
+            mean, med = time_delta(xd, reps=max(10, args.steps // 2), warmup=3,
                                    warm_s=min(args.warm_seconds, 1.0))
             gbs = work["delta_bytes"] / (mean * 1e-3) / 1e9
             hbm_lines["delta"] = {"ms": round(mean, 4), "ms_median": round(med, 4),
                                   "GB/s": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                   "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                                   "bytes": work["delta_bytes"],
-                                  "note": "fa_bwd_delta on this workload's shape (reads O and dO, "
+                                  "shape": list(xd.shape),
+                                  "note": "fa_bwd_delta on this shape (reads O and dO, "
                                           "writes delta; the bf16 fa_bwd forms delta in dQ): 30 "
                                           "back-to-back calls over 6 buffer pairs, per call"}
             log(f"delta kernel: {hbm_lines['delta']}")
@@ -539,6 +563,11 @@ def main():
         roof["measured_peak"] = measured[w.dtype] if w.dtype in measured else None
         if roof["unit"] == "TFLOP/s" and roof["measured_peak"]:
             roof["frac_of_measured_peak"] = round(roof["achieved"] / roof["measured_peak"], 4)
+        for x in fwdbwd.values():
+            r = x["roofline"]
+            if r["unit"] == "TFLOP/s" and measured.get("bf16"):
+                r["measured_peak"] = measured["bf16"]
+                r["frac_of_measured_peak"] = round(r["achieved"] / measured["bf16"], 4)
         for name, x in extra.items():
             dt = "fp8" if name.startswith(("fp8", "mxfp8")) else "bf16"
             if "TFLOP/s" in x and dt in measured:
@@ -563,6 +592,7 @@ def main():
         "frac_of_peak": round(value / peak, 4),
         "kernels": kernels,
         "roofline": roof,
+        "fwdbwd_workloads": fwdbwd,
         "forward_workloads": extra,
         "bias_workloads": bias_lines,
         "hbm_kernels": hbm_lines,

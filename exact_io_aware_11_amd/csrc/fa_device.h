@@ -57,10 +57,12 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Raw buffer resource over `bytes` bytes at `base`.  Buffer loads at byte
 // offsets past the end do not touch memory and deliver zeros (also into LDS),
 // which is how tiles running past the sequence end are padded.
-// num_records is a 32-bit unsigned field: byte counts up to 2^32 - 1 (callers
-// keep them below that) go in as their bit pattern.
+// num_records is a 32-bit unsigned field.  Longer extents saturate at
+// 2^32 - 1: every resource here starts at the tile it serves and is read at
+// offsets far below 2^32, so for those reads a saturated bound is as good as
+// the true one (a wrapped count would turn in-range rows into zeros).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
-  const uint32_t n = bytes > 0 ? (uint32_t)bytes : 0u;
+  const uint32_t n = bytes <= 0 ? 0u : bytes >= 0xFFFFFFFFL ? 0xFFFFFFFFu : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
                                            __builtin_bit_cast(int, n), 0x00020000);
 }

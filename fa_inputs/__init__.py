@@ -205,6 +205,22 @@ def make_inputs(shape, dtype: str, seed: int = 42, with_dout: bool = True) -> In
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def device_normal_bf16(shape, seed: int, count: int = 3):
+    """`count` bf16 tensors of `shape` on the current GPU, N(0, 1) float32
+    draws from torch's seeded device generator rounded to nearest even.  For
+    sequences too long to draw on the host in reasonable time; the oracle gets
+    the exact values by copying (parts of) these tensors back."""
+    import torch
+
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    out = []
+    for _ in range(count):
+        x = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+        out.append(x.to(torch.bfloat16))
+        del x
+    return out
+
+
 def pitch(n: int) -> int:
     """A row pitch for an n-key bias row: n rounded up to a multiple of 4 (the
     strides the library takes), plus 4 so that the pitch always differs from n."""

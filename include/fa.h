@@ -27,12 +27,13 @@
  *  - Causal: key j is visible to query i iff j <= i (square attention).
  *  - LSE_i = ln sum_j exp(S_ij) in the natural log of the scaled scores.
  *  - All pointers are device pointers the caller owns.  The library allocates
- *    nothing, keeps no mutable global state and never synchronises: work is
- *    enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
- *    call returns.  Calls on different streams are independent.
- *  - Supported head sizes d: 64 and 128.  Any N >= 1; B * H * N == 0 is a
- *    no-op returning FA_OK.  Tensor pointers must be 16-byte aligned, LSE and
- *    workspace 4-byte aligned.  B*H*N*d must stay below 2^40 elements.
+ *    nothing and never synchronises: work is enqueued on `stream` (a
+ *    hipStream_t; NULL = the default stream) and the call returns.  Calls on
+ *    different streams are independent.  No mutable global state is kept.
+ *  - Supported head sizes d: 64 and 128.  Any N >= 1 (a head's K or V may
+ *    exceed 4 GiB); B * H * N == 0 is a no-op returning FA_OK.  Tensor
+ *    pointers must be 16-byte aligned, LSE and workspace 4-byte aligned.
+ *    B*H*N*d must stay below 2^40 elements.
  *  - scale must be finite and > 0.
  *  - Errors: argument problems return FA_ERR_INVALID_ARG or FA_ERR_UNSUPPORTED
  *    before anything is launched; a failed launch returns FA_ERR_HIP.  No
@@ -117,8 +118,10 @@ fa_status fa_fwd_bias(const void* q, const void* k, const void* v, const float* 
                       void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
                       int dtype, void* stream);
 
-/* Bytes of device workspace fa_bwd needs for these sizes (delta, one float32
- * per row, at the start of the workspace).  Returns 0 for invalid sizes. */
+/* Bytes of device workspace fa_bwd needs for these sizes: delta_i =
+ * dO_i . O_i of "FlashAttention-1: eliminating IO", section 10.2.4, one
+ * float32 per row at the start of the workspace, rounded up to 256 bytes.
+ * Returns 0 for invalid sizes (nothing is checked beyond the sizes). */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
 /* Backward pass ("FlashAttention-1: eliminating IO", section 10.2.4).
@@ -187,7 +190,8 @@ fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const float* 
  * blocks 1..65536, iters 1..2^20. */
 fa_status fa_measure_mfma_rate(float* out, int blocks, int iters, int dtype, void* stream);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
+/* Static, NUL-terminated description of a status code (never NULL).  The
+ * pages define no error convention; the codes are this library's own. */
 const char* fa_status_string(int status);
 
 #ifdef __cplusplus

@@ -16,7 +16,7 @@ import oracle
 # every format: |err| <= atol + rtol |LSE_ref| elementwise; the rtol term
 # covers the float32 accumulation of large scores in the matrix cores.
 TOL = {"fp32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
-LSE_TOL = {"fp32": (1e-5, 0.0), "bf16": (1e-3, 1e-5), "fp8": (1e-2, 1e-4)}
+LSE_TOL = {"fp32": (1e-5, 0.0), "bf16": (1e-3, 1e-5), "fp8": (1e-3, 1e-5)}
 SCALE_FLOOR = 1e-3
 
 
@@ -93,6 +93,40 @@ def run_bwd(dev_qkv, o, lse, inp, scale, causal, prefill_nan=True):
     torch.cuda.synchronize()
     delta = ws[: B * H * N * 4].view(torch.float32).view(B, H, N)
     return grads, delta
+
+
+def rows_by_key_chunks(q_rows, rows, scale, chunk, N, fetch):
+    """Oracle rows of one head whose keys are too many to hold in float64 at
+    once.  For each query row r (causal: keys 0..r), the oracle's forward runs
+    on consecutive key chunks of at most `chunk` keys without a mask, and the
+    chunk results are merged by the two-partition rule of "FlashAttention-1:
+    eliminating IO", section 10.2.2: LSE = ln sum_c exp(LSE_c) and
+    O = sum_c exp(LSE_c - LSE) O_c.  fetch(a, b) returns the exact float64 K
+    and V rows a..b-1; q_rows[i] is the float64 query of rows[i].  Returns
+    (O [R, d], LSE [R])."""
+    d = q_rows.shape[1]
+    o_out = np.zeros((len(rows), d))
+    lse_out = np.zeros(len(rows))
+    end = max(rows) + 1
+    parts = [[] for _ in rows]
+    for a in range(0, min(end, N), chunk):
+        b = min(a + chunk, end)
+        kc, vc = fetch(a, b)
+        for i, r in enumerate(rows):
+            if r < a:
+                continue
+            n = min(b, r + 1) - a
+            qbuf = np.zeros((n, d))
+            qbuf[0] = q_rows[i]
+            o_c, lse_c = oracle.attn_fwd_rows(qbuf, kc[:n], vc[:n], [0], scale, False)
+            parts[i].append((o_c[0], lse_c[0]))
+    for i, p in enumerate(parts):
+        lses = np.array([x[1] for x in p])
+        top = lses.max()
+        lse = top + np.log(np.sum(np.exp(lses - top)))
+        o_out[i] = sum(np.exp(l - lse) * o for o, l in p)
+        lse_out[i] = lse
+    return o_out, lse_out
 
 
 def rel_err(got, ref):

@@ -14,7 +14,8 @@ import pytest
 
 import fa_inputs
 import oracle
-from _util import check, exact_values, run_bwd, run_fwd, say, to_f64
+from _util import (LSE_TOL, TOL, check, exact_values, rel_err, rows_by_key_chunks, run_bwd,
+                   run_fwd, say, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,18 +100,40 @@ def test_fp8_fwd_small(N, d, causal):
 # --------------------------------------------------------------------------- #
 # The four large workloads at full size: sampled rows / heads against the oracle
 # --------------------------------------------------------------------------- #
-def sampled_fwd_check(w, heads, rows, seed=42):
+def sampled_fwd_check(w, heads, rows, seed=42, block=256):
+    """The workload at full size in the launch configuration bench.py times:
+    `rows` of the listed heads, and in EVERY (b, h) six rows -- the first and
+    last rows of the first row block, the first row of the second, a row that
+    moves with the head index, and the last two rows -- against the oracle's
+    rows (each costs one pass over the head's keys)."""
     inp = fa_inputs.make_inputs(w.shape, w.dtype, seed=seed, with_dout=False)
     dev, o, lse = run_fwd(inp, w.scale, w.causal)
     o_all, lse_all = to_f64(o), to_f64(lse)
     assert np.isfinite(o_all).all() and np.isfinite(lse_all).all()
+
+    def exact_head(b, h):
+        return (exact_values(x[b, h], w.dtype, s)
+                for x, s in zip((inp.q, inp.k, inp.v), inp.descale))
+
     for (b, h) in heads:
-        qs, ks, vs = (exact_values(x[b, h], w.dtype, s)
-                      for x, s in zip((inp.q, inp.k, inp.v), inp.descale))
-        o_ref, lse_ref = oracle.attn_fwd_rows(qs, ks, vs, rows, w.scale, w.causal)
+        o_ref, lse_ref = oracle.attn_fwd_rows(*exact_head(b, h), rows, w.scale, w.causal)
         check(f"{w.name} head ({b},{h}) O rows", o_all[b, h, rows], o_ref, w.dtype)
         check(f"{w.name} head ({b},{h}) LSE rows", lse_all[b, h, rows], lse_ref, w.dtype,
               lse=True)
+    worst_o = worst_l = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            bh = b * w.H + h
+            every = np.unique([0, block - 1, block, (977 * bh + 131) % w.N, w.N - 2, w.N - 1])
+            o_ref, lse_ref = oracle.attn_fwd_rows(*exact_head(b, h), every, w.scale, w.causal)
+            worst_o = max(worst_o, rel_err(o_all[b, h, every], o_ref))
+            atol, rtol = LSE_TOL[w.dtype]
+            worst_l = max(worst_l, float(np.max(np.abs(lse_all[b, h, every] - lse_ref)
+                                                - (atol + rtol * np.abs(lse_ref)))))
+            assert rel_err(o_all[b, h, every], o_ref) <= TOL[w.dtype], (b, h)
+    say(f"{w.name}: all {w.B * w.H} heads, 6 rows each: worst O err {worst_o:.3e}, "
+        f"worst LSE excess over its bar {worst_l:.3e}")
+    assert worst_l <= 0
     return inp, dev, o, lse
 
 
@@ -122,17 +145,17 @@ def sample_rows(N, n=24, seed=0):
 
 def test_full_bf16_fwd_b4h16n2048d64():
     w = fa_inputs.WORKLOADS["bf16_fwd_b4h16n2048d64"]
-    sampled_fwd_check(w, [(0, 0), (3, 15), (2, 7)], sample_rows(w.N))
+    sampled_fwd_check(w, [(0, 0), (3, 15), (2, 7)], sample_rows(w.N), block=128)
 
 
 def test_full_bf16_causal_fwd_b2h32n8192d128():
     w = fa_inputs.WORKLOADS["bf16_causal_fwd_b2h32n8192d128"]
-    sampled_fwd_check(w, [(0, 0), (1, 31), (0, 17)], sample_rows(w.N))
+    sampled_fwd_check(w, [(0, 0), (1, 31), (0, 17)], sample_rows(w.N), block=256)
 
 
 def test_full_fp8_fwd_b1h32n16384d128():
     w = fa_inputs.WORKLOADS["fp8_fwd_b1h32n16384d128"]
-    sampled_fwd_check(w, [(0, 0), (0, 31)], sample_rows(w.N, n=16))
+    sampled_fwd_check(w, [(0, 0), (0, 31)], sample_rows(w.N, n=16), block=128)
 
 
 def test_full_bf16_causal_fwd_bwd_b2h16n4096d128():
@@ -270,6 +293,40 @@ def test_longest_sequence_forward(dtype, d, causal):
     check(f"{dtype} N=2^17 d={d} causal={causal} O rows", o_all[0, 0, rows], o_ref, dtype)
     check(f"{dtype} N=2^17 d={d} causal={causal} LSE rows", lse_all[0, 0, rows], lse_ref, dtype,
           lse=True)
+
+
+def test_per_head_extent_beyond_4gib():
+    """N = 2^24 keys at d = 128 in bf16: one head's K and V are 4 GiB each, so
+    the byte extent from a tile to the head's end no longer fits the 32-bit
+    record count of a buffer resource (it saturates; a wrapped count would
+    read the first tiles as zeros).  Causal forward (about a minute on the
+    GPU); rows of the first two 256-row blocks and of the middle against the
+    oracle on the key prefix they see, the last rows by key chunks."""
+    N, d = 1 << 24, 128
+    scale = 1 / math.sqrt(d)
+    say("N=2^24 d=128 causal: drawing inputs on the GPU")
+    q, k, v = fa_inputs.device_normal_bf16((1, 1, N, d), seed=24)
+    o = torch.full((1, 1, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((1, 1, N), float("nan"), dtype=torch.float32, device="cuda")
+    say("N=2^24 d=128 causal: forward")
+    fa.fa_fwd(q, k, v, o, lse, scale, True)
+    torch.cuda.synchronize()
+    say("N=2^24 d=128 causal: checking rows")
+
+    def exact(t, a, b):
+        return oracle.decode_bf16(t[0, 0, a:b].cpu().view(torch.int16).numpy().view(np.uint16))
+
+    head = [0, 1, 63, 64, 255, 256, 300, 511]
+    o_ref, lse_ref = oracle.attn_fwd_rows(exact(q, 0, 512), exact(k, 0, 512), exact(v, 0, 512),
+                                          head, scale, True)
+    check("N=2^24 first blocks O", to_f64(o[0, 0, head]), o_ref, "bf16")
+    check("N=2^24 first blocks LSE", to_f64(lse[0, 0, head]), lse_ref, "bf16", lse=True)
+    tail = [(1 << 21) + 77, N - 257, N - 2, N - 1]
+    qr = np.stack([exact(q, r, r + 1)[0] for r in tail])
+    o_ref, lse_ref = rows_by_key_chunks(qr, tail, scale, 1 << 21, N,
+                                        lambda a, b: (exact(k, a, b), exact(v, a, b)))
+    check("N=2^24 middle and last rows O", to_f64(o[0, 0, tail]), o_ref, "bf16")
+    check("N=2^24 middle and last rows LSE", to_f64(lse[0, 0, tail]), lse_ref, "bf16", lse=True)
 
 
 def test_many_heads_fwd_bwd():
