@@ -8,6 +8,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_FP32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_NOALLOC_MAX_ROWS = 1 << 22  # include/fa.h
 
 # The entry points include/fa.h declares, with their ctypes signatures.
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -22,6 +23,8 @@ SIGNATURES = {
                          _i, _vp]),
     "fa_bwd_bias": (_i, [_vp, _vp, _vp, _vp, _ll, _ll, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _sz, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "fa_bwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i,
+                            _i, _vp]),
     "fa_measure_mfma_rate": (_i, [_vp, _i, _i, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
 }

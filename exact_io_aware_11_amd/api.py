@@ -209,6 +209,28 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale: float, causal: b
     _bwd_call("fa_bwd", q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream)
 
 
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool, stream=None):
+    """fa_bwd without a workspace: delta lives in the library's per-GPU scratch
+    (B*H*N <= FA_NOALLOC_MAX_ROWS; calls that overlap on one GPU race on it).
+    Writes dq, dk, dv, bitwise as fa_bwd does."""
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _check_like(name, t, (B, H, N, d))
+    _check_like("lse", lse, (B, H, N))
+    code = dtype_code(q)
+    if code == FA_FP8_E4M3:
+        raise FAError(2, "fa_bwd_noalloc: the backward takes float32 or bfloat16 tensors")
+    _check_dtypes(code, (("k", k), ("v", v), ("o", o), ("dout", dout)),
+                  (("dq", dq), ("dk", dk), ("dv", dv)))
+    st = lib.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), code,
+                            _stream_handle(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_noalloc: " + fa_status_string(st))
+
+
 def fa_bwd_delta(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream=None):
     """Backward stage: delta into the workspace (fa_bwd runs it for float32;
     for bf16 the dQ stage forms delta itself)."""
@@ -264,5 +286,5 @@ def flops_bwd(B, H, N, d, causal) -> float:
 
 __all__ = ["FA_FP32", "FA_BF16", "FA_FP8_E4M3", "dtype_code", "fa_fwd", "fa_fwd_bias",
            "fa_fwd_mxfp8", "fa_bwd", "fa_bwd_bias",
-           "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
+           "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_noalloc",
            "fa_bwd_workspace_size", "fa_status_string", "flops_fwd", "flops_bwd"]

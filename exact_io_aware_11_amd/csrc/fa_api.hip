@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_kernels.h"
 
@@ -166,44 +168,45 @@ namespace {
 
 enum { kStageDelta = 1, kStageDkDv = 2, kStageDq = 4 };
 
-fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
-                  size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
-                  int dtype, void* stream, int stages, const fa::Bias& bias = fa::Bias{}) {
+// Validation shared by the backward entry points (all but the workspace).
+// Fills *a except a->delta; *empty is set when there is no work.
+fa_status prepare_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                      int H, int N, int d, float scale, int causal, int dtype, void* stream,
+                      const fa::Bias& bias, fa::BwdArgs* a, bool* empty) {
   if (dtype != FA_FP32 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-  bool empty = false;
-  fa_status st = check_sizes(B, H, N, d, &empty);
+  fa_status st = check_sizes(B, H, N, d, empty);
   if (st != FA_OK) return st;
   if (dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
   if (!finite_pos(scale)) return FA_ERR_INVALID_ARG;
-  if (empty) return FA_OK;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
-    return FA_ERR_INVALID_ARG;
+  if (*empty) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4) || !aligned(workspace, 4))
+      !aligned(lse, 4))
     return FA_ERR_INVALID_ARG;
-  if (workspace_bytes < ws_bytes((long)B * H, N)) return FA_ERR_INVALID_ARG;
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->o = o;
+  a->dout = dout;
+  a->lse = lse;
+  a->dq = dq;
+  a->dk = dk;
+  a->dv = dv;
+  a->delta = nullptr;
+  a->BH = (long)B * H;
+  a->N = N;
+  a->d = d;
+  a->scale = scale;
+  a->causal = causal != 0;
+  a->bias = bias;
+  a->stream = (hipStream_t)stream;
+  return FA_OK;
+}
 
-  fa::BwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.dout = dout;
-  a.lse = lse;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.delta = (float*)workspace;
-  a.BH = (long)B * H;
-  a.N = N;
-  a.d = d;
-  a.scale = scale;
-  a.causal = causal != 0;
-  a.bias = bias;
-  a.stream = (hipStream_t)stream;
+fa_status launch_bwd(const fa::BwdArgs& a, int dtype, int stages) {
   hipError_t e = hipSuccess;
   if (dtype == FA_BF16) {
     // The bf16 dQ kernel forms delta itself and stores it for the dK/dV
@@ -217,6 +220,21 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
     if (e == hipSuccess && (stages & kStageDq)) e = fa::launch_dq_f32(a);
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                  int dtype, void* stream, int stages, const fa::Bias& bias = fa::Bias{}) {
+  fa::BwdArgs a;
+  bool empty = false;
+  const fa_status st = prepare_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
+                                   dtype, stream, bias, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!workspace || !aligned(workspace, 4)) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_bytes((long)B * H, N)) return FA_ERR_INVALID_ARG;
+  a.delta = (float*)workspace;
+  return launch_bwd(a, dtype, stages);
 }
 
 }  // namespace
@@ -248,6 +266,61 @@ fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const float* 
   const fa_status st = check_bias(bias, bias_stride_b, bias_stride_h, bias_stride_q, H, N, &b);
   if (st != FA_OK) return st;
   return run_bwd(FA_BWD_ARGS, kStageDelta | kStageDkDv | kStageDq, b);
+}
+
+}  // extern "C"
+
+// The allocation-free backward keeps delta (one float per row) in this
+// device-global array instead of a caller's workspace.  Every GPU the library
+// runs on holds its own copy, at its own address, until the process ends.  In
+// host code the array's name is only a stand-in: its device address is looked
+// up per device (once, with that device current) and only that address is
+// handed to kernels.
+static __device__ __align__(256) float scratch[FA_NOALLOC_MAX_ROWS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, which must be the
+// device of `stream` (the null stream: the current device).
+fa_status scratch_address(void* stream, float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return FA_ERR_HIP;
+    if (sdev != dev) return FA_ERR_INVALID_ARG;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+  fa::BwdArgs a;
+  bool empty = false;
+  fa_status st = prepare_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
+                             stream, fa::Bias{}, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  if ((long)B * (long)H * (long)N > (long)FA_NOALLOC_MAX_ROWS) return FA_ERR_UNSUPPORTED;
+  st = scratch_address(stream, &a.delta);
+  if (st != FA_OK) return st;
+  return launch_bwd(a, dtype, kStageDelta | kStageDkDv | kStageDq);
 }
 
 fa_status fa_measure_mfma_rate(float* out, int blocks, int iters, int dtype, void* stream) {

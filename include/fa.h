@@ -29,7 +29,8 @@
  *  - All pointers are device pointers the caller owns.  The library allocates
  *    nothing and never synchronises: work is enqueued on `stream` (a
  *    hipStream_t; NULL = the default stream) and the call returns.  Calls on
- *    different streams are independent.  No mutable global state is kept.
+ *    different streams are independent.  The only mutable global state is the
+ *    per-device scratch of fa_bwd_noalloc (see there).
  *  - Supported head sizes d: 64 and 128.  Any N >= 1 (a head's K or V may
  *    exceed 4 GiB); B * H * N == 0 is a no-op returning FA_OK.  Tensor
  *    pointers must be 16-byte aligned, LSE and workspace 4-byte aligned.
@@ -175,6 +176,32 @@ fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const float* 
                       const void* o, const void* dout, const float* lse, void* dq, void* dk,
                       void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N,
                       int d, float scale, int causal, int dtype, void* stream);
+
+/* Largest B * H * N that fa_bwd_noalloc accepts: its delta scratch holds one
+ * float32 per row, 16 MiB per GPU. */
+#define FA_NOALLOC_MAX_ROWS (1 << 22)
+
+/* fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same computation, kernels and outputs as fa_bwd
+ * (bitwise), same arguments minus workspace and workspace_bytes.  delta lives
+ * in a device-global array of FA_NOALLOC_MAX_ROWS floats that the library
+ * image holds on each GPU it runs on until the process ends; its contents
+ * after a call are that call's delta.
+ *  - B * H * N > FA_NOALLOC_MAX_ROWS returns FA_ERR_UNSUPPORTED (nothing is
+ *    launched); the other argument errors are fa_bwd's.
+ *  - The current device must be the device of `stream` (FA_ERR_INVALID_ARG
+ *    otherwise).  The first call on a device looks the array's address up in
+ *    the runtime (no allocation by this library); make that first call
+ *    outside stream capture.
+ *  - All calls on one GPU share the array: calls that overlap in time on one
+ *    GPU (different streams without ordering, or several host threads) race
+ *    on it and give undefined results.  Calls ordered on one stream are
+ *    safe.  Nothing in the array needs clearing: every call writes delta
+ *    before reading it. */
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 /* Measurement aid, not part of attention: enqueues a pure stream of 32x32
  * matrix-core products (bf16 32x32x16 or fp8 32x32x64, FLOPs per product

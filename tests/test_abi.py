@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_bias", "fa_bwd_delta", "fa_bwd_dkdv",
-                                    "fa_bwd_dq", "fa_bwd_workspace_size", "fa_fwd",
+                                    "fa_bwd_dq", "fa_bwd_noalloc", "fa_bwd_workspace_size",
+                                    "fa_fwd",
                                     "fa_fwd_bias", "fa_fwd_mxfp8", "fa_measure_mfma_rate",
                                     "fa_status_string"]
 
@@ -147,6 +148,33 @@ def test_bwd_rejects_before_launch(kw, status, fn):
 
 def test_bwd_empty_is_a_noop():
     assert bwd(N=0) == OK and bwd(B=0, q=0) == OK
+
+
+def bwd_noalloc(**kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, H=1, N=16, d=64,
+             scale=0.125, causal=0, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return lib.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                              a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                              a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_FP8_E4M3), UNSUPPORTED), (dict(d=80), UNSUPPORTED),
+    (dict(dtype=9), INVALID), (dict(causal=-1), INVALID), (dict(scale=0.0), INVALID),
+    (dict(do=0), INVALID), (dict(dq=0), INVALID), (dict(dk=P + 4), INVALID),
+    (dict(lse=P + 2), INVALID), (dict(B=-1), INVALID),
+    # beyond the scratch: one row too many, in several splits of B * H * N
+    (dict(N=fa.FA_NOALLOC_MAX_ROWS + 1), UNSUPPORTED),
+    (dict(B=2, H=8, N=fa.FA_NOALLOC_MAX_ROWS // 16 + 1), UNSUPPORTED),
+    (dict(B=1 << 11, H=1 << 11, N=2), UNSUPPORTED),
+])
+def test_bwd_noalloc_rejects_before_launch(kw, status):
+    assert bwd_noalloc(**kw) == status
+
+
+def test_bwd_noalloc_empty_is_a_noop():
+    assert bwd_noalloc(N=0) == OK and bwd_noalloc(B=0, q=0) == OK
 
 
 @pytest.mark.parametrize("args,status", [
