@@ -73,18 +73,18 @@ def source_hash(stage: str) -> str:
 
 
 def measured_traffic(workload: str, stage: str):
-    """HBM bytes per launch of `stage` from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE, scaled by a copy-kernel calibration),
-    or None if it was taken on other sources of that kernel or another
-    workload."""
+    """HBM bytes per launch of `stage` on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a
+    copy-kernel calibration), or None if none was taken for that pair or it
+    was taken on other sources of that kernel."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    st = t.get("stages", {}).get(stage)
-    if t.get("workload") != workload or st is None or stage not in STAGE_SOURCES:
+    st = t.get("workloads", {}).get(workload, {}).get("stages", {}).get(stage)
+    if st is None or stage not in STAGE_SOURCES:
         return None
     if st.get("source_sha256") != source_hash(stage):
         return None
@@ -374,6 +374,50 @@ def time_bias(shape, causal, kind, window, backward, reps, warmup, warm_s=0.0):
     return out
 
 
+IO_COMPARE = ["bf16_fwd_b4h16n2048d64", "bf16_causal_fwdbwd_b2h16n4096d128"]
+
+
+def time_io_compare(reps, warmup, warm_s=0.0):
+    """The forward by fa_fwd (S and P stay on chip) and by fa_std_fwd, the
+    standard attention that writes S (float32) and P (bf16) to device memory
+    and reads them back, on the same inputs.  Returns per-workload times and
+    the algorithmic device-memory bytes of each: Q, K, V read once, O and LSE
+    written once, plus for the standard form S written and read and P written
+    and read (N x ldp entries per head)."""
+    import torch
+
+    import exact_io_aware_11_amd as fa
+    import fa_inputs
+
+    out = {}
+    for name in IO_COMPARE:
+        w = fa_inputs.WORKLOADS[name]
+        _, q, k, v, _ = device_inputs(w, False)
+        B, H, N, d = w.shape
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(fa.fa_std_workspace_size(B, H, N, d), dtype=torch.uint8, device="cuda")
+        f_mean, f_med = time_calls(lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal), reps,
+                                   warmup, warm_s)
+        s_mean, s_med = time_calls(
+            lambda: fa.fa_std_fwd(q, k, v, o, lse, ws, w.scale, w.causal), reps, warmup, warm_s)
+        ldp = (N + 63) // 64 * 64
+        io = 4 * B * H * N * d * 2 + 4 * B * H * N  # Q, K, V, O (bf16) and LSE
+        nn = B * H * N * ldp
+        std_io = io + 2 * nn * 4 + 2 * nn * 2      # + S written, read; P written, read
+        flops = fa.flops_fwd(B, H, N, d, w.causal)
+        out[name] = {"flash_ms": round(f_mean, 4), "flash_ms_median": round(f_med, 4),
+                     "flash_TFLOP/s": round(flops / (f_mean * 1e-3) / 1e12, 1),
+                     "standard_ms": round(s_mean, 4), "standard_ms_median": round(s_med, 4),
+                     "standard_TFLOP/s": round(flops / (s_mean * 1e-3) / 1e12, 1),
+                     "speedup": round(s_mean / f_mean, 2),
+                     "algorithmic_bytes_flash": io, "algorithmic_bytes_standard": std_io}
+        log(f"io comparison {name}: {out[name]}")
+        del q, k, v, o, lse, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, max_heads):
     """The oracle as it stands on a bounded sample: whole heads of the workload."""
     import numpy as np
@@ -472,6 +516,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads the CPU oracle runs (0: all B*H heads of the workload)")
+    ap.add_argument("--io-compare", action="store_true",
+                    help="only time fa_fwd against the standard attention fa_std_fwd (S and P "
+                         "in device memory) on the two IO-comparison workloads")
     ap.add_argument("--hbm-calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -489,6 +536,11 @@ def main():
 
     import exact_io_aware_11_amd as fa  # noqa: F401  (fails loudly without libfa.so)
     import fa_inputs
+
+    if args.io_compare:
+        print(json.dumps({"io_comparison": time_io_compare(max(3, args.steps), args.warmup)}),
+              flush=True)
+        return
 
     w = fa_inputs.WORKLOADS[args.workload]
     log(f"workload {w.name} steps={args.steps} warmup={args.warmup}")
@@ -556,6 +608,11 @@ def main():
                                           "back-to-back calls over 6 buffer pairs, per call"}
             log(f"delta kernel: {hbm_lines['delta']}")
 
+    io_cmp = None
+    if not args.no_extra:
+        io_cmp = time_io_compare(reps=max(5, args.steps // 4), warmup=2,
+                                 warm_s=min(args.warm_seconds, 0.5))
+
     measured = None
     if not args.no_extra or args.rate_probe:
         measured = measure_mfma_rates()
@@ -596,6 +653,7 @@ def main():
         "forward_workloads": extra,
         "bias_workloads": bias_lines,
         "hbm_kernels": hbm_lines,
+        "io_comparison": io_cmp,
         "mfma_rate_measured": None if measured is None else dict(
             measured, unit="TFLOP/s",
             note="pure 32x32 matrix-core products on pseudo-random operands, every CU, warm "

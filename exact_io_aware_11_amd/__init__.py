@@ -14,6 +14,8 @@ C names:
   the library's per-GPU scratch instead of a workspace
 * :func:`fa_bwd_delta`, :func:`fa_bwd_dkdv`, :func:`fa_bwd_dq` -- fa_bwd's stages,
   separately (for bf16 the dQ stage also writes delta)
+* :func:`fa_std_fwd`, :func:`fa_std_workspace_size` -- standard attention with
+  S and P written to device memory: the baseline of the IO comparison
 * :func:`fa_bwd_workspace_size`, :func:`fa_status_string`
 * :func:`fa_measure_mfma_rate` -- a measurement aid: the matrix-core rate on
   realistic operand bits, against which the kernels' rates are also read
@@ -28,12 +30,13 @@ from ._lib import (FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, 
 from .api import (dtype_code, fa_bwd, fa_bwd_bias, fa_bwd_delta, fa_bwd_dkdv, fa_bwd_dq,
                   fa_bwd_noalloc,
                   fa_bwd_workspace_size, fa_fwd, fa_fwd_bias, fa_fwd_mxfp8, fa_measure_mfma_rate,
-                  fa_status_string, flops_bwd, flops_fwd)
+                  fa_status_string, fa_std_fwd, fa_std_workspace_size, flops_bwd, flops_fwd)
 
 __all__ = [
     "FA_FP32", "FA_BF16", "FA_FP8_E4M3", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",
     "FA_ERR_HIP", "FAError", "lib", "fa_fwd", "fa_fwd_bias", "fa_fwd_mxfp8", "fa_bwd",
     "fa_bwd_bias", "fa_bwd_delta", "fa_bwd_dkdv", "fa_measure_mfma_rate",
     "fa_bwd_dq", "fa_bwd_noalloc", "FA_NOALLOC_MAX_ROWS", "fa_bwd_workspace_size",
+    "fa_std_fwd", "fa_std_workspace_size",
     "fa_status_string", "dtype_code", "flops_fwd", "flops_bwd",
 ]

@@ -17,6 +17,8 @@ SIGNATURES = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _f, _f, _f, _vp]),
     "fa_fwd_mxfp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]),
     "fa_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "fa_std_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "fa_std_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _f,
                     _i, _i, _vp]),
     "fa_fwd_bias": (_i, [_vp, _vp, _vp, _vp, _ll, _ll, _ll, _vp, _vp, _i, _i, _i, _i, _f, _i,

@@ -176,6 +176,33 @@ def fa_bwd_bias(q, k, v, bias, o, dout, lse, dq, dk, dv, workspace, scale: float
         raise FAError(st, "fa_bwd_bias: " + fa_status_string(st))
 
 
+def fa_std_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(lib.fa_std_workspace_size(B, H, N, d))
+
+
+def fa_std_fwd(q, k, v, o, lse, workspace, scale: float, causal: bool, stream=None):
+    """Enqueue standard attention with S and P written to the workspace (uint8
+    device tensor of fa_std_workspace_size bytes, 256-byte aligned): the
+    materialising baseline of the IO comparison.  bf16 only; writes o, lse."""
+    import torch
+
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_like(name, t, (B, H, N, d))
+    _check_like("lse", lse, (B, H, N))
+    code = dtype_code(q)
+    _check_dtypes(code, (("k", k), ("v", v)), (("o", o),))
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    _check_device("workspace", workspace)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_std_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        workspace.data_ptr(), nbytes, B, H, N, d, float(scale),
+                        int(bool(causal)), code, _stream_handle(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_std_fwd: " + fa_status_string(st))
+
+
 def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(lib.fa_bwd_workspace_size(B, H, N, d))
 
@@ -287,4 +314,5 @@ def flops_bwd(B, H, N, d, causal) -> float:
 __all__ = ["FA_FP32", "FA_BF16", "FA_FP8_E4M3", "dtype_code", "fa_fwd", "fa_fwd_bias",
            "fa_fwd_mxfp8", "fa_bwd", "fa_bwd_bias",
            "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_noalloc",
-           "fa_bwd_workspace_size", "fa_status_string", "flops_fwd", "flops_bwd"]
+           "fa_bwd_workspace_size", "fa_std_fwd", "fa_std_workspace_size", "fa_status_string",
+           "flops_fwd", "flops_bwd"]

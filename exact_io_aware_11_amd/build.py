@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libfa.so")
 SOURCES = ["fa_api.hip", "fwd_bf16.hip", "fwd_fp8.hip", "f32_kernels.hip", "bwd_bf16.hip",
-           "peak_probe.hip"]
+           "std_attn.hip", "peak_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are switched off for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

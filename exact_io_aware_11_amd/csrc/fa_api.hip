@@ -156,6 +156,53 @@ fa_status fa_fwd_mxfp8(const void* q, const void* k, const void* v, const void* 
   return fa::launch_fwd_fp8(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_std_workspace_size(int B, int H, int N, int d) {
+  bool empty = false;
+  if (check_sizes(B, H, N, d, &empty) != FA_OK) return 0;
+  const size_t ldp = ((size_t)N + 63) / 64 * 64;
+  const size_t entries = (size_t)B * (size_t)H * (size_t)N * ldp;
+  return (entries * 4 + 255) / 256 * 256 + (entries * 2 + 255) / 256 * 256;
+}
+
+fa_status fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                     float scale, int causal, int dtype, void* stream) {
+  if (dtype != FA_FP32 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  bool empty = false;
+  const fa_status st = check_sizes(B, H, N, d, &empty);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!finite_pos(scale)) return FA_ERR_INVALID_ARG;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 256))
+    return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_std_workspace_size(B, H, N, d)) return FA_ERR_INVALID_ARG;
+  // grids: 64 x 64 score tiles by B*H (the second and third grid dimensions
+  // stay within 65535), one softmax workgroup per four rows
+  if ((long)B * H > 65535 || (N + 63) / 64 > 65535) return FA_ERR_UNSUPPORTED;
+  if (((long)B * H * N + 3) / 4 > 0x7fffffffL) return FA_ERR_INVALID_ARG;
+  fa::StdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = (long)B * H;
+  a.N = N;
+  a.d = d;
+  a.ldp = (N + 63) / 64 * 64;
+  a.scale = scale;
+  a.causal = causal != 0;
+  const size_t entries = (size_t)a.BH * (size_t)N * (size_t)a.ldp;
+  a.s = static_cast<float*>(workspace);
+  a.p = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + (entries * 4 + 255) / 256 * 256);
+  a.stream = (hipStream_t)stream;
+  return fa::launch_std_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   bool empty = false;
   if (check_sizes(B, H, N, d, &empty) != FA_OK) return 0;

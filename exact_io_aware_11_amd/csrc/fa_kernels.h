@@ -58,6 +58,23 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// Standard attention with S and P materialised in device memory (bf16 inputs):
+// S float32 and P bfloat16, [BH][N][ldp] each, ldp = N rounded up to 64.
+struct StdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* s;
+  uint16_t* p;
+  long BH;
+  int N, d, ldp;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_fp8(const FwdArgs& a);
@@ -66,6 +83,7 @@ hipError_t launch_dkdv_f32(const BwdArgs& a);
 hipError_t launch_dq_f32(const BwdArgs& a);
 hipError_t launch_dkdv_bf16(const BwdArgs& a);
 hipError_t launch_dq_bf16(const BwdArgs& a);  // also writes delta (from O and dO)
+hipError_t launch_std_bf16(const StdArgs& a);
 hipError_t launch_mfma_peak(float* out, int blocks, int iters, bool fp8, hipStream_t stream);
 
 }  // namespace fa

@@ -119,6 +119,27 @@ fa_status fa_fwd_bias(const void* q, const void* k, const void* v, const float* 
                       void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
                       int dtype, void* stream);
 
+/* Standard attention, the baseline the pages measure the IO-aware method
+ * against (reading notes "5.4 FlashAttention (1/2/3)", standard attention;
+ * explainer, background section): S = scale Q K^T is written to device
+ * memory in float32, a row-wise softmax reads it and writes P in bfloat16,
+ * and O = P V reads P back -- O(N^2) bytes of device-memory traffic per head
+ * where fa_fwd moves O(N d).  Same result as fa_fwd up to rounding (P is
+ * normalised before the product), for measuring that difference; it is not
+ * an alternative implementation of the library's path.
+ *   q, k, v, o, lse, scale, causal : as fa_fwd; dtype must be FA_BF16
+ *             (FA_FP32 and FA_FP8_E4M3 return FA_ERR_UNSUPPORTED)
+ *   workspace : 256-byte aligned device buffer of at least
+ *             fa_std_workspace_size() bytes; on return it holds S
+ *             ([B,H,N,ldp] float32, ldp = N rounded up to 64) followed (at
+ *             the next 256-byte boundary) by P ([B,H,N,ldp] bfloat16, zero
+ *             where masked and in the padding)
+ * B*H must stay below 65536 and N below 2^22 (FA_ERR_UNSUPPORTED). */
+size_t fa_std_workspace_size(int B, int H, int N, int d);
+fa_status fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                     float scale, int causal, int dtype, void* stream);
+
 /* Bytes of device workspace fa_bwd needs for these sizes: delta_i =
  * dO_i . O_i of "FlashAttention-1: eliminating IO", section 10.2.4, one
  * float32 per row at the start of the workspace, rounded up to 256 bytes.

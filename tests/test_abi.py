@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
                                     "fa_bwd_dq", "fa_bwd_noalloc", "fa_bwd_workspace_size",
                                     "fa_fwd",
                                     "fa_fwd_bias", "fa_fwd_mxfp8", "fa_measure_mfma_rate",
-                                    "fa_status_string"]
+                                    "fa_status_string", "fa_std_fwd", "fa_std_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -183,6 +183,34 @@ def test_bwd_noalloc_empty_is_a_noop():
     ((P, 256, 10, 0), UNSUPPORTED), ((P, 256, 10, 7), INVALID)])
 def test_rate_probe_rejects_before_launch(args, status):
     assert lib.fa_measure_mfma_rate(*args, None) == status
+
+
+def std(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, ws=P, wsb=1 << 30, B=1, H=1, N=16, d=64, scale=0.125,
+             causal=0, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return lib.fa_std_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["wsb"], a["B"],
+                          a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+                          a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(dtype=fa.FA_FP8_E4M3), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED), (dict(dtype=7), INVALID), (dict(causal=2), INVALID),
+    (dict(scale=0.0), INVALID), (dict(q=0), INVALID), (dict(ws=0), INVALID),
+    (dict(ws=P + 16), INVALID), (dict(o=P + 4), INVALID), (dict(wsb=100), INVALID),
+    (dict(B=1 << 9, H=1 << 8, wsb=1 << 62), UNSUPPORTED),
+])
+def test_std_rejects_before_launch(kw, status):
+    assert std(**kw) == status
+
+
+def test_std_workspace_size():
+    # S float32 and P bf16, rows padded to 64 entries, each part 256-byte rounded
+    assert lib.fa_std_workspace_size(1, 1, 16, 64) == 16 * 64 * 4 + 2048
+    assert lib.fa_std_workspace_size(2, 3, 100, 128) == 6 * 100 * 128 * 4 + 6 * 100 * 128 * 2
+    assert lib.fa_std_workspace_size(1, 1, 3, 96) == 0
+    assert std(N=0) == OK and std(B=0, ws=0) == OK
 
 
 def test_workspace_size():
