@@ -224,6 +224,38 @@ def test_large_magnitude_scores(causal):
     full_check_bwd(inp, 1 / math.sqrt(128), causal, "bf16 50x Q")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["growing", "jump", "jump_big_v"])
+def test_scores_that_outgrow_the_first_tile(kind, causal, d):
+    """Rows whose largest scores lie far beyond their first key tile: keys
+    grow along the sequence (each later tile moves the row's reference up),
+    or one late key scores so much higher that exp of its score against the
+    first tile's maximum overflows float32, also with values large enough
+    that P V overflows before any rescaling.  The result is still the exact
+    softmax (against the oracle)."""
+    N = 700
+    rng = np.random.default_rng(31 + d + int(causal))
+    q = rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    k = rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    v = rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    if kind == "growing":
+        q = np.abs(q) + 0.5
+        k = np.abs(k) * np.linspace(0.2, 3.0, N, dtype=np.float32)[None, None, :, None]
+    else:
+        big = np.arange(300, N, 97)  # a few late keys, one per row block or so
+        q[...] = np.abs(q) + 1.0
+        # "jump": scores ~12 d E|q| past the first tile's maximum, so far that
+        # exp against it overflows; "jump_big_v": 2^110 .. 2^126 times that
+        # maximum (finite), with values of 2^20 that make P V overflow
+        k[:, :, big, :] = 12.0 if kind == "jump" else (4.3 if d == 128 else 6.1)
+        if kind == "jump_big_v":
+            v[:, :, big, :] *= 2.0 ** 20
+    do = rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    inp = bf16_inputs_from(q, k, v, do)
+    full_check_fwd(inp, 1 / math.sqrt(d), causal, f"bf16 {kind} d={d}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_runs_are_bitwise_deterministic(dtype):
     inp = fa_inputs.make_inputs((2, 4, 700, 128), dtype, seed=10)
