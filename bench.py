@@ -266,6 +266,54 @@ def time_fwd_only(w, reps, warmup, warm_s=0.0):
     return res
 
 
+SCHEDULES = ["interleaved", "pingpong", "rows64"]
+
+
+def time_schedules(reps, rounds=3, warm_s=0.5):
+    """The forward schedules (FA_FWD_SCHEDULE) on the headline shape, causal
+    and not: the same inputs, the schedules timed in turn for `rounds` rounds
+    of `reps` back-to-back calls (so clock drift hits all alike); per schedule
+    the median of its rounds' means."""
+    import statistics
+
+    import torch
+
+    import exact_io_aware_11_amd as fa
+    import fa_inputs
+
+    w = fa_inputs.WORKLOADS[MAIN]
+    inp, q, k, v, _ = device_inputs(w, False)
+    o = torch.empty(w.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.shape[:3], dtype=torch.float32, device="cuda")
+    out = {}
+    saved = os.environ.get("FA_FWD_SCHEDULE")
+    try:
+        for causal in (True, False):
+            ms = {sched: [] for sched in SCHEDULES}
+            for r in range(rounds):
+                for sched in SCHEDULES:
+                    os.environ["FA_FWD_SCHEDULE"] = sched
+                    mean, _ = time_calls(
+                        lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, causal, descale=inp.descale),
+                        reps, 2, warm_s if r == 0 else 0.0)
+                    ms[sched].append(mean)
+            flops = fa.flops_fwd(w.B, w.H, w.N, w.d, causal)
+            name = w.name if causal else w.name.replace("_causal", "")
+            out[name] = {}
+            for sched in SCHEDULES:
+                m = statistics.median(ms[sched])
+                out[name][sched] = {"ms": round(m, 4),
+                                    "TFLOP/s": round(flops / (m * 1e-3) / 1e12, 1)}
+    finally:
+        if saved is None:
+            os.environ.pop("FA_FWD_SCHEDULE", None)
+        else:
+            os.environ["FA_FWD_SCHEDULE"] = saved
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_mfma_rates(warm_s=0.5, reps=10):
     """The matrix-core rate on realistic operand bits (fa_measure_mfma_rate:
     pure 32x32 products on pseudo-random per-lane data, two waves per SIMD on
@@ -609,9 +657,12 @@ def main():
             log(f"delta kernel: {hbm_lines['delta']}")
 
     io_cmp = None
+    schedules = None
     if not args.no_extra:
         io_cmp = time_io_compare(reps=max(5, args.steps // 4), warmup=2,
                                  warm_s=min(args.warm_seconds, 0.5))
+        schedules = time_schedules(reps=max(5, args.steps // 4))
+        log(f"forward schedules: {schedules}")
 
     measured = None
     if not args.no_extra or args.rate_probe:
@@ -645,7 +696,8 @@ def main():
                                   "workload's format",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "passes": "fwd+bwd" if w.backward else "fwd",
-                   "scale": w.scale, "parallelism": "single GPU"},
+                   "scale": w.scale, "parallelism": "single GPU",
+                   "forward_schedule": os.environ.get("FA_FWD_SCHEDULE") or "interleaved"},
         "frac_of_peak": round(value / peak, 4),
         "kernels": kernels,
         "roofline": roof,
@@ -654,6 +706,7 @@ def main():
         "bias_workloads": bias_lines,
         "hbm_kernels": hbm_lines,
         "io_comparison": io_cmp,
+        "forward_schedules": schedules,
         "mfma_rate_measured": None if measured is None else dict(
             measured, unit="TFLOP/s",
             note="pure 32x32 matrix-core products on pseudo-random operands, every CU, warm "

@@ -17,8 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.hip", "fwd_bf16.hip", "fwd_fp8.hip", "f32_kernels.hip", "bwd_bf16.hip",
-           "std_attn.hip", "peak_probe.hip"]
+SOURCES = ["fa_api.hip", "fwd_bf16.hip", "fwd_bf16_pp.hip", "fwd_bf16_w64.hip", "fwd_fp8.hip",
+           "f32_kernels.hip", "bwd_bf16.hip", "std_attn.hip", "peak_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are switched off for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -31,8 +31,11 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # operands and fuses into three-input max instructions.
 # In the backward kernels the score accumulators are read by vector ALU ops
 # every tile; asking the compiler to keep matrix-core results in ordinary VGPRs
-# (not accumulation registers) saves one register move per element.
+# (not accumulation registers) saves one register move per element.  The same
+# holds for the 64-rows-per-wave forward, which needs the whole register file.
 FILE_FLAGS = {"fwd_bf16.hip": ["-fno-honor-nans"], "fwd_fp8.hip": ["-fno-honor-nans"],
+              "fwd_bf16_pp.hip": ["-fno-honor-nans"],
+              "fwd_bf16_w64.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
               "bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 

@@ -3,6 +3,8 @@
 // anything.  See include/fa.h for the contract.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -58,6 +60,16 @@ size_t ws_bytes(long BH, int N) {
   return (delta + 255) & ~(size_t)255;
 }
 
+// FA_FWD_SCHEDULE (read on every call): unset, empty or "interleaved", the
+// default; "pingpong" or "rows64".  Anything else: -1.
+int fwd_schedule() {
+  const char* s = getenv("FA_FWD_SCHEDULE");
+  if (!s || !*s || !strcmp(s, "interleaved")) return fa::kSchedInterleaved;
+  if (!strcmp(s, "pingpong")) return fa::kSchedPingPong;
+  if (!strcmp(s, "rows64")) return fa::kSchedRows64;
+  return -1;
+}
+
 fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int N, int d, float scale, int causal, int dtype, float q_descale,
                   float k_descale, float v_descale, const fa::Bias& bias, void* stream) {
@@ -70,6 +82,8 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
   if (dtype == FA_FP8_E4M3 &&
       (!finite_pos(q_descale) || !finite_pos(k_descale) || !finite_pos(v_descale)))
     return FA_ERR_INVALID_ARG;
+  const int schedule = fwd_schedule();
+  if (schedule < 0) return FA_ERR_INVALID_ARG;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
@@ -91,6 +105,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
   a.k_descale = k_descale;
   a.v_descale = v_descale;
   a.bias = bias;
+  a.schedule = schedule;
   a.stream = (hipStream_t)stream;
   hipError_t e;
   switch (dtype) {

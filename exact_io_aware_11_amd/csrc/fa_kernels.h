@@ -19,6 +19,15 @@ struct Bias {
   uint32_t head_bytes = 0;
 };
 
+// Forward schedules of the bf16 d = 128 kernels without a bias (the
+// FA_FWD_SCHEDULE environment variable): the same results, different ways of
+// overlapping the matrix products with the softmax arithmetic.
+enum FwdSchedule : int {
+  kSchedInterleaved = 0,  // fwd_bf16.hip: softmax woven into the next tile's products
+  kSchedPingPong = 1,     // fwd_bf16_pp.hip: two wave groups alternate products and softmax
+  kSchedRows64 = 2,       // fwd_bf16_w64.hip: 64 rows per wave, one wave per SIMD
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -36,6 +45,7 @@ struct FwdArgs {
   const uint8_t* k_scale = nullptr;
   const uint8_t* v_scale = nullptr;
   Bias bias;  // p == nullptr: none
+  int schedule = kSchedInterleaved;  // bf16, d = 128, no bias
   hipStream_t stream;
 };
 
@@ -77,6 +87,8 @@ struct StdArgs {
 
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_bf16_pp(const FwdArgs& a);   // d = 128, no bias
+hipError_t launch_fwd_bf16_w64(const FwdArgs& a);  // d = 128, no bias
 hipError_t launch_fwd_fp8(const FwdArgs& a);
 hipError_t launch_delta(const BwdArgs& a, bool bf16);
 hipError_t launch_dkdv_f32(const BwdArgs& a);

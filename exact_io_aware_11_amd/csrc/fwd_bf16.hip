@@ -619,6 +619,8 @@ static hipError_t launch_fwd_bf16_b(const FwdArgs& a) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
   if (a.d == 64) return a.causal ? launch_fwd_bf16_b<64, true>(a) : launch_fwd_bf16_b<64, false>(a);
+  if (!a.bias.p && a.schedule == kSchedPingPong) return launch_fwd_bf16_pp(a);
+  if (!a.bias.p && a.schedule == kSchedRows64) return launch_fwd_bf16_w64(a);
   return a.causal ? launch_fwd_bf16_b<128, true>(a) : launch_fwd_bf16_b<128, false>(a);
 }
 

@@ -71,7 +71,16 @@ typedef enum {
  *   q_descale, k_descale, v_descale : fp8 only -- the real value of a code c
  *             is decode(c) * descale (one scale per tensor, finite, > 0);
  *             ignored for the other formats.
- * Accumulation is float32 for every format. */
+ * Accumulation is float32 for every format.
+ * Schedule (bf16, d = 128, no bias; read from the environment variable
+ * FA_FWD_SCHEDULE on every fa_fwd and fa_fwd_bias call): unset, empty or
+ * "interleaved" -- the default, each wave weaves a tile's softmax into the
+ * next tile's matrix products; "pingpong" -- two wave groups per SIMD
+ * alternate products and softmax (the reading notes' three-generation table,
+ * FA3 ping-pong scheduling); "rows64" -- 64 query rows per wave, one wave per
+ * SIMD.  All three compute the same outputs up to rounding (their float32
+ * additions run in different orders); any other
+ * value returns FA_ERR_INVALID_ARG. */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, int dtype, float q_descale,
                  float k_descale, float v_descale, void* stream);

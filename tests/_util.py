@@ -154,3 +154,97 @@ def check(name, got, ref, dtype, lse=False):
         say(f"{name}: max err / max|ref| {e:.3e} (tol {TOL[dtype]:.0e})")
         assert e <= TOL[dtype], f"{name}: {e}"
     return e
+
+
+def full_check_fwd(inp, scale, causal, tag):
+    say(f"{tag}: fwd {inp.dtype} shape={inp.q.shape} causal={causal}")
+    dev, o, lse = run_fwd(inp, scale, causal)
+    qs, ks, vs = (exact_values(x, inp.dtype, s) for x, s in zip((inp.q, inp.k, inp.v), inp.descale))
+    o_ref, lse_ref = oracle.attn_fwd(qs, ks, vs, scale, causal)
+    check(f"{tag} O", to_f64(o), o_ref, inp.dtype)
+    check(f"{tag} LSE", to_f64(lse), lse_ref, inp.dtype, lse=True)
+    return dev, o, lse, (qs, ks, vs)
+
+
+def bf16_inputs_from(q, k, v, do=None):
+    return fa_inputs.Inputs(fa_inputs.to_bf16_bits(q), fa_inputs.to_bf16_bits(k),
+                            fa_inputs.to_bf16_bits(v),
+                            None if do is None else fa_inputs.to_bf16_bits(do), (1., 1., 1.),
+                            "bf16")
+
+
+# Inputs whose largest scores lie far beyond the first key tile of their rows.
+#  growing     keys grow along the sequence: each later tile moves the row's
+#              reference up
+#  jump        a few late keys score ~12 d E|q| above the first tile's maximum,
+#              so far that exp against that maximum overflows float32
+#  jump_big_v  late keys 2^110 .. 2^126 times the first tile's maximum in
+#              probability (finite), their values times 2^20: P V overflows
+#              before any rescaling
+#  jump_huge_v late keys ~2^40 times it (row sums stay below 2^64), their
+#              values times 2^100: P V overflows while the row sum does not
+OUTGROW_KINDS = ["growing", "jump", "jump_big_v", "jump_huge_v"]
+
+
+def outgrow_inputs(kind, causal, d, N=700):
+    rng = np.random.default_rng(31 + d + int(causal))
+    q = rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    k = rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    v = rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    if kind == "growing":
+        q = np.abs(q) + 0.5
+        k = np.abs(k) * np.linspace(0.2, 3.0, N, dtype=np.float32)[None, None, :, None]
+    else:
+        big = np.arange(300, N, 97)  # a few late keys, one per row block or so
+        q[...] = np.abs(q) + 1.0
+        k[:, :, big, :] = {"jump": 12.0, "jump_big_v": 4.3 if d == 128 else 6.1,
+                           "jump_huge_v": 1.46 if d == 128 else 2.07}[kind]
+        if kind == "jump_big_v":
+            v[:, :, big, :] *= 2.0 ** 20
+        if kind == "jump_huge_v":
+            v[:, :, big, :] *= 2.0 ** 100
+    do = rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    return bf16_inputs_from(q, k, v, do)
+
+
+def sampled_fwd_check(w, heads, rows, seed=42, block=256):
+    """The workload at full size in the launch configuration bench.py times:
+    `rows` of the listed heads, and in EVERY (b, h) six rows -- the first and
+    last rows of the first row block, the first row of the second, a row that
+    moves with the head index, and the last two rows -- against the oracle's
+    rows (each costs one pass over the head's keys)."""
+    inp = fa_inputs.make_inputs(w.shape, w.dtype, seed=seed, with_dout=False)
+    dev, o, lse = run_fwd(inp, w.scale, w.causal)
+    o_all, lse_all = to_f64(o), to_f64(lse)
+    assert np.isfinite(o_all).all() and np.isfinite(lse_all).all()
+
+    def exact_head(b, h):
+        return (exact_values(x[b, h], w.dtype, s)
+                for x, s in zip((inp.q, inp.k, inp.v), inp.descale))
+
+    for (b, h) in heads:
+        o_ref, lse_ref = oracle.attn_fwd_rows(*exact_head(b, h), rows, w.scale, w.causal)
+        check(f"{w.name} head ({b},{h}) O rows", o_all[b, h, rows], o_ref, w.dtype)
+        check(f"{w.name} head ({b},{h}) LSE rows", lse_all[b, h, rows], lse_ref, w.dtype,
+              lse=True)
+    worst_o = worst_l = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            bh = b * w.H + h
+            every = np.unique([0, block - 1, block, (977 * bh + 131) % w.N, w.N - 2, w.N - 1])
+            o_ref, lse_ref = oracle.attn_fwd_rows(*exact_head(b, h), every, w.scale, w.causal)
+            worst_o = max(worst_o, rel_err(o_all[b, h, every], o_ref))
+            atol, rtol = LSE_TOL[w.dtype]
+            worst_l = max(worst_l, float(np.max(np.abs(lse_all[b, h, every] - lse_ref)
+                                                - (atol + rtol * np.abs(lse_ref)))))
+            assert rel_err(o_all[b, h, every], o_ref) <= TOL[w.dtype], (b, h)
+    say(f"{w.name}: all {w.B * w.H} heads, 6 rows each: worst O err {worst_o:.3e}, "
+        f"worst LSE excess over its bar {worst_l:.3e}")
+    assert worst_l <= 0
+    return inp, dev, o, lse
+
+
+def sample_rows(N, n=24, seed=0):
+    r = np.random.default_rng(seed).choice(N, size=n, replace=False)
+    edge = [0, 1, 31, 32, 63, 64, 127, 128, N // 2, N - 2, N - 1]
+    return np.unique(np.concatenate([r, edge]))

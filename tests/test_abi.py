@@ -135,6 +135,16 @@ def test_fwd_empty_is_a_noop(kw):
     assert fwd(**kw) == OK
 
 
+@pytest.mark.parametrize("name,status", [("", OK), ("interleaved", OK), ("pingpong", OK),
+                                         ("rows64", OK), ("ping-pong", INVALID), ("w64", INVALID)])
+def test_fwd_schedule_names(monkeypatch, name, status):
+    """FA_FWD_SCHEDULE is read on every forward call and an unknown name is
+    rejected before any launch (an empty problem launches nothing anyway)."""
+    monkeypatch.setenv("FA_FWD_SCHEDULE", name)
+    assert fwd(B=0) == status
+    assert fwd_b(B=0) == status
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=fa.FA_FP8_E4M3), UNSUPPORTED), (dict(d=80), UNSUPPORTED),
     (dict(dtype=9), INVALID), (dict(causal=-1), INVALID), (dict(scale=0.0), INVALID),

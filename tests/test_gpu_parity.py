@@ -4,8 +4,8 @@ the same seeded inputs (the oracle consumes the exact values the GPU gets).
 Bars: float32 -- max abs error <= 1e-5 on every output; bf16 -- max error
 <= 2e-2 * max|oracle| per tensor (O, dQ, dK, dV); fp8 -- 6e-2 * max|oracle|
 (O).  LSE (float32 in every format): |err| <= 1e-5 (fp32), 1e-3 + 1e-5|LSE|
-(bf16), 1e-2 + 1e-4|LSE| (fp8).  Outputs are prefilled with NaN, so an
-unwritten element fails.
+(bf16 and fp8).  Outputs are prefilled with NaN, so an unwritten element
+fails.
 """
 import math
 
@@ -14,8 +14,9 @@ import pytest
 
 import fa_inputs
 import oracle
-from _util import (LSE_TOL, TOL, check, exact_values, rel_err, rows_by_key_chunks, run_bwd,
-                   run_fwd, say, to_f64)
+from _util import (OUTGROW_KINDS, bf16_inputs_from, check, exact_values, full_check_fwd,
+                   outgrow_inputs, rows_by_key_chunks, run_bwd, run_fwd, sample_rows,
+                   sampled_fwd_check, say, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,16 +25,6 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("no GPU", allow_module_level=True)
 
 import exact_io_aware_11_amd as fa  # noqa: E402  (loads libfa.so; fails loudly if missing)
-
-
-def full_check_fwd(inp, scale, causal, tag):
-    say(f"{tag}: fwd {inp.dtype} shape={inp.q.shape} causal={causal}")
-    dev, o, lse = run_fwd(inp, scale, causal)
-    qs, ks, vs = (exact_values(x, inp.dtype, s) for x, s in zip((inp.q, inp.k, inp.v), inp.descale))
-    o_ref, lse_ref = oracle.attn_fwd(qs, ks, vs, scale, causal)
-    check(f"{tag} O", to_f64(o), o_ref, inp.dtype)
-    check(f"{tag} LSE", to_f64(lse), lse_ref, inp.dtype, lse=True)
-    return dev, o, lse, (qs, ks, vs)
 
 
 def full_check_bwd(inp, scale, causal, tag):
@@ -100,49 +91,6 @@ def test_fp8_fwd_small(N, d, causal):
 # --------------------------------------------------------------------------- #
 # The four large workloads at full size: sampled rows / heads against the oracle
 # --------------------------------------------------------------------------- #
-def sampled_fwd_check(w, heads, rows, seed=42, block=256):
-    """The workload at full size in the launch configuration bench.py times:
-    `rows` of the listed heads, and in EVERY (b, h) six rows -- the first and
-    last rows of the first row block, the first row of the second, a row that
-    moves with the head index, and the last two rows -- against the oracle's
-    rows (each costs one pass over the head's keys)."""
-    inp = fa_inputs.make_inputs(w.shape, w.dtype, seed=seed, with_dout=False)
-    dev, o, lse = run_fwd(inp, w.scale, w.causal)
-    o_all, lse_all = to_f64(o), to_f64(lse)
-    assert np.isfinite(o_all).all() and np.isfinite(lse_all).all()
-
-    def exact_head(b, h):
-        return (exact_values(x[b, h], w.dtype, s)
-                for x, s in zip((inp.q, inp.k, inp.v), inp.descale))
-
-    for (b, h) in heads:
-        o_ref, lse_ref = oracle.attn_fwd_rows(*exact_head(b, h), rows, w.scale, w.causal)
-        check(f"{w.name} head ({b},{h}) O rows", o_all[b, h, rows], o_ref, w.dtype)
-        check(f"{w.name} head ({b},{h}) LSE rows", lse_all[b, h, rows], lse_ref, w.dtype,
-              lse=True)
-    worst_o = worst_l = 0.0
-    for b in range(w.B):
-        for h in range(w.H):
-            bh = b * w.H + h
-            every = np.unique([0, block - 1, block, (977 * bh + 131) % w.N, w.N - 2, w.N - 1])
-            o_ref, lse_ref = oracle.attn_fwd_rows(*exact_head(b, h), every, w.scale, w.causal)
-            worst_o = max(worst_o, rel_err(o_all[b, h, every], o_ref))
-            atol, rtol = LSE_TOL[w.dtype]
-            worst_l = max(worst_l, float(np.max(np.abs(lse_all[b, h, every] - lse_ref)
-                                                - (atol + rtol * np.abs(lse_ref)))))
-            assert rel_err(o_all[b, h, every], o_ref) <= TOL[w.dtype], (b, h)
-    say(f"{w.name}: all {w.B * w.H} heads, 6 rows each: worst O err {worst_o:.3e}, "
-        f"worst LSE excess over its bar {worst_l:.3e}")
-    assert worst_l <= 0
-    return inp, dev, o, lse
-
-
-def sample_rows(N, n=24, seed=0):
-    r = np.random.default_rng(seed).choice(N, size=n, replace=False)
-    edge = [0, 1, 31, 32, 63, 64, 127, 128, N // 2, N - 2, N - 1]
-    return np.unique(np.concatenate([r, edge]))
-
-
 def test_full_bf16_fwd_b4h16n2048d64():
     w = fa_inputs.WORKLOADS["bf16_fwd_b4h16n2048d64"]
     sampled_fwd_check(w, [(0, 0), (3, 15), (2, 7)], sample_rows(w.N), block=128)
@@ -183,13 +131,6 @@ def test_full_bf16_causal_fwd_bwd_b2h16n4096d128():
 # --------------------------------------------------------------------------- #
 # Edge cases and special inputs
 # --------------------------------------------------------------------------- #
-def bf16_inputs_from(q, k, v, do=None):
-    return fa_inputs.Inputs(fa_inputs.to_bf16_bits(q), fa_inputs.to_bf16_bits(k),
-                            fa_inputs.to_bf16_bits(v),
-                            None if do is None else fa_inputs.to_bf16_bits(do), (1., 1., 1.),
-                            "bf16")
-
-
 @pytest.mark.parametrize("causal", [False, True])
 def test_zero_queries_average_values(causal):
     q, k, v, do = fa_inputs.draw_f32((1, 2, 300, 128), seed=5)
@@ -226,34 +167,13 @@ def test_large_magnitude_scores(causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("kind", ["growing", "jump", "jump_big_v"])
+@pytest.mark.parametrize("kind", OUTGROW_KINDS)
 def test_scores_that_outgrow_the_first_tile(kind, causal, d):
-    """Rows whose largest scores lie far beyond their first key tile: keys
-    grow along the sequence (each later tile moves the row's reference up),
-    or one late key scores so much higher that exp of its score against the
-    first tile's maximum overflows float32, also with values large enough
-    that P V overflows before any rescaling.  The result is still the exact
-    softmax (against the oracle)."""
-    N = 700
-    rng = np.random.default_rng(31 + d + int(causal))
-    q = rng.standard_normal((1, 2, N, d)).astype(np.float32)
-    k = rng.standard_normal((1, 2, N, d)).astype(np.float32)
-    v = rng.standard_normal((1, 2, N, d)).astype(np.float32)
-    if kind == "growing":
-        q = np.abs(q) + 0.5
-        k = np.abs(k) * np.linspace(0.2, 3.0, N, dtype=np.float32)[None, None, :, None]
-    else:
-        big = np.arange(300, N, 97)  # a few late keys, one per row block or so
-        q[...] = np.abs(q) + 1.0
-        # "jump": scores ~12 d E|q| past the first tile's maximum, so far that
-        # exp against it overflows; "jump_big_v": 2^110 .. 2^126 times that
-        # maximum (finite), with values of 2^20 that make P V overflow
-        k[:, :, big, :] = 12.0 if kind == "jump" else (4.3 if d == 128 else 6.1)
-        if kind == "jump_big_v":
-            v[:, :, big, :] *= 2.0 ** 20
-    do = rng.standard_normal((1, 2, N, d)).astype(np.float32)
-    inp = bf16_inputs_from(q, k, v, do)
-    full_check_fwd(inp, 1 / math.sqrt(d), causal, f"bf16 {kind} d={d}")
+    """Rows whose largest scores lie far beyond their first key tile (see
+    outgrow_inputs): the result is still the exact softmax (against the
+    oracle)."""
+    full_check_fwd(outgrow_inputs(kind, causal, d), 1 / math.sqrt(d), causal,
+                   f"bf16 {kind} d={d}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
