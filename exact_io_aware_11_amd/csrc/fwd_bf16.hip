@@ -73,13 +73,13 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  // per block of a pair: set when the FAST path must be redone (zeroed here,
-  // before the first barrier of the first block)
-  __shared__ int redo[2];
+  // set when the FAST path must be redone (zeroed here, before the block's
+  // first barrier)
+  __shared__ int redo[1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (tid < 2) redo[tid] = 0;
+  if (tid == 0) redo[0] = 0;
   const int g = lane >> 5, r32 = lane & 31;
   // Causal: a workgroup takes row blocks u and n_qblk - 1 - u, which together
   // visit the same number of key tiles for every u, so all workgroups carry
@@ -563,34 +563,28 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   return bad;
   };  // body
 
-  // One block: the FAST path, and if any lane of the workgroup reports a
-  // non-finite row sum or accumulator, the SAFE path again on the same block
-  // (it overwrites the block's outputs).  Ends at a barrier, so the next
-  // block may restage the LDS tiles.  With a bias, and under the causal mask,
-  // the SAFE path alone: on causal blocks the FAST path measured 2 % slower
-  // at N = 4096 and no faster at N = 8192, on full rows 2-3 % faster.
+  // With a bias, and under the causal mask, the SAFE path alone: on causal
+  // blocks the FAST path measured 2 % slower at N = 4096 and no faster at
+  // N = 8192, on full rows 2-3 % faster.  Otherwise the FAST path, and if any
+  // lane of the workgroup reports a non-finite row sum or accumulator, the
+  // SAFE path again on the same block (it overwrites the block's outputs).
   using FASTC = std::true_type;
   using SAFEC = std::false_type;
-  auto run = [&](uint32_t qblk, int slot) __attribute__((always_inline)) {
-    if constexpr (BIAS || CAUSAL) {
-      body(qblk, SAFEC{});
-      barrier_vm<0>();
-    } else {
-      const bool bad = body(qblk, FASTC{});
-      if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo[slot] = 1;
-      barrier_vm<0>();
-      if (redo[slot] != 0) {  // uniform over the workgroup
-        body(qblk, SAFEC{});
-        barrier_vm<0>();
-      }
-    }
-  };
   if constexpr (CAUSAL) {
     const uint32_t partner = n_qblk - 1 - unit;
-    run(partner, 0);  // the longer block first
-    if (partner != unit) run(unit, 1);  // (uniform over the workgroup)
+    body(partner, SAFEC{});  // the longer block first
+    if (partner != unit) {  // uniform over the workgroup
+      barrier_vm<0>();  // every wave is done with the first block's LDS tiles
+      body(unit, SAFEC{});
+    }
+  } else if constexpr (BIAS) {
+    body(unit, SAFEC{});
   } else {
-    run(unit, 0);
+    const bool bad = body(unit, FASTC{});
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo[0] = 1;
+    barrier_vm<0>();  // (also: every wave is done with the LDS tiles)
+    if (redo[0] != 0)  // uniform over the workgroup
+      body(unit, SAFEC{});
   }
 }
 
