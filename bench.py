@@ -536,6 +536,8 @@ def step_report(w, ms, per):
         else:
             tf = work[s] / (t * 1e-3) / 1e12
             kernels[s] = {"ms": round(t, 4), "TFLOP/s": round(tf, 1), "frac": round(tf / peak, 4)}
+            if s == "dq":  # it also recomputes S and dP: three products executed, one credited
+                kernels[s]["executed_TFLOP/s"] = round(3 * tf, 1)
     dom = max(per, key=per.get)
     if dom == "delta":
         ach = work["delta_bytes"] / (per[dom] * 1e-3) / 1e9
