@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     else return lo1;
   };
   auto tile_rsrc = [&](const uint16_t* src, int row0) {
-    return make_rsrc(src + (size_t)row0 * D, (long)(N - row0) * (2 * D));
+    return make_tile_rsrc<2 * D>(src + (size_t)row0 * D, N - row0);
   };
   auto stage_one = [&](const __amdgpu_buffer_rsrc_t& qr, const __amdgpu_buffer_rsrc_t& orr,
                        auto bufc, int L) {
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     ldoff[x] = (uint32_t)(row * 2 * D + ((((byte % (2 * D)) >> 4) ^ swz<D>(row)) << 4));
   }
   auto tile_rsrc = [&](const uint16_t* src, int key0) {
-    return make_rsrc(src + (size_t)key0 * D, (long)(N - key0) * (2 * D));
+    return make_tile_rsrc<2 * D>(src + (size_t)key0 * D, N - key0);
   };
   // Load L (0 .. 2 LPW - 1): piece L / 2 of K (L even) or of V (L odd).
   auto stage_one = [&](const __amdgpu_buffer_rsrc_t& kr, const __amdgpu_buffer_rsrc_t& vr,

@@ -66,6 +66,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
                                            __builtin_bit_cast(int, n), 0x00020000);
 }
+// The same for a tile of `rows` rows of ROW_BYTES bytes (rows may be <= 0),
+// saturated in 32-bit arithmetic: rows past the largest count that fits
+// 2^32 - 1 bytes give 2^32 - 1.  (The 64-bit form of make_rsrc moved the
+// register allocation of the dQ kernel with a bias into heavy spilling.)
+template <int ROW_BYTES>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_tile_rsrc(const void* base, int rows) {
+  constexpr int kMaxRows = (int)(0xFFFFFFFFu / ROW_BYTES);
+  const uint32_t n =
+      rows <= 0 ? 0u : rows >= kMaxRows ? 0xFFFFFFFFu : (uint32_t)rows * (uint32_t)ROW_BYTES;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           __builtin_bit_cast(int, n), 0x00020000);
+}
 // Loads into registers through a buffer resource (reads past num_records
 // return zeros): 16 or 4 bytes per lane at voff + soff + imm.
 template <int IMM = 0>
