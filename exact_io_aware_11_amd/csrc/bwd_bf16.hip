@@ -522,6 +522,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const int key0 = j * BN;
     const auto kr = tile_rsrc(Kh, key0 + BN);
     const auto vr = tile_rsrc(Vh, key0 + BN);
+    // Masked tiles: the lane id formed here, once per tile, rather than a
+    // row index held in a register through the whole scan (which spilled).
+    [[maybe_unused]] int ln_m = 0;
+    if constexpr (masked) ln_m = lane_id_here();
     constexpr int NA = 2 * NT, NB = 2 * NCB, DEPTH = 4;
     auto fetch_a = [&](int b, int k) -> bf16x8 {  // k-th product of G_A(b)
       const uint16_t* base = ((k & 1) ? Vt : Kt) + 32 * D * b;
@@ -544,14 +548,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     auto soft_elem = [&](int b, int i) {  // key of element i: key0 + 32 b + 8 (i / 4) + 4 g + i % 4
       float p = exp2_fast(fmaf(s[b][i], scale_log2, -lse2));
       if constexpr (masked && BIAS) {
-        const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3);
-        if ((CAUSAL && key > qrow) || key >= N) p = 0.f;
-      } else if constexpr (masked) {  // causal only: the lane index is recomputed here, so no
-        // register is held across the whole scan for the mask (a spill and a full memory wait
-        // in the diagonal tiles otherwise)
-        const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-        const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * (ln >> 5) + (i & 3);
-        if (key > q0 + (ln & 31)) p = 0.f;
+        const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * (ln_m >> 5) + (i & 3);
+        if ((CAUSAL && key > q0 + (ln_m & 31)) || key >= N) p = 0.f;
+      } else if constexpr (masked) {  // causal only
+        const int key = key0 + 32 * b + 8 * (i >> 2) + 4 * (ln_m >> 5) + (i & 3);
+        if (key > q0 + (ln_m & 31)) p = 0.f;
       }
       dp[b][i] = p * (dp[b][i] - del);
       if ((i & 7) == 7) db[b][i >> 3] = to_bf16x8(dp[b], i - 7);
@@ -659,8 +660,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   }
   wait_vm<0>();  // the last (unused) loads land before the workgroup's LDS is released
 
-  if (qrow < N) {
-    uint16_t* dQrow = dQ + head + (size_t)qrow * D;
+  // (the row is formed again from the lane id: keeping it, or the row
+  // address, live through the tile loops costs a spilled register)
+  const int ln_e = lane_id_here();
+  const int qrow_e = q0 + (ln_e & 31), g_e = ln_e >> 5;
+  if (qrow_e < N) {
+    uint16_t* dQrow = dQ + head + (size_t)qrow_e * D;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -668,7 +673,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (__bf16)(adq[cb][4 * q4 + e] * scale);
-        *reinterpret_cast<bf16x4*>(dQrow + 32 * cb + 8 * q4 + 4 * g) = v;
+        *reinterpret_cast<bf16x4*>(dQrow + 32 * cb + 8 * q4 + 4 * g_e) = v;
       }
   }
 }

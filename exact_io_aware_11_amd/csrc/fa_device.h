@@ -54,6 +54,15 @@ __device__ __forceinline__ f32x16 mfma_fp8_scaled(i32x8 a, i32x8 b, f32x16 c, ui
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// This lane's index in the wave, computed where it is used: the asm is not
+// merged with other computations of the lane id or hoisted out of a loop, so
+// no register holds it (or values derived from it) across a long scan.
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Raw buffer resource over `bytes` bytes at `base`.  Buffer loads at byte
 // offsets past the end do not touch memory and deliver zeros (also into LDS),
 // which is how tiles running past the sequence end are padded.
