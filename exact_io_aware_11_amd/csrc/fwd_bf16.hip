@@ -92,11 +92,14 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
 
-  // FAST (no bias, no causal mask): the reference max is taken on the block's first tile
-  // only; afterwards each tile's probabilities, formed against the current
-  // reference, are checked through their row sum (see settle).  SAFE: the
-  // row max of every tile before its probabilities are formed.  Returns
-  // (per lane) whether the block must be recomputed on the SAFE path.
+  // FAST (no bias, no causal mask): the reference max is taken on the
+  // block's first tile only and kept.  Later probabilities exp(S - m) may
+  // exceed 1 by anything float32 holds, which costs no relative precision,
+  // and need no per-tile max.  A block whose row sum ends at 2^64 or beyond
+  // (or not finite), or whose accumulator is not finite (P V past the float
+  // range), is recomputed on the SAFE path.  SAFE: the row max of every tile
+  // before its probabilities are formed (lazy rescale).  Returns (per lane)
+  // whether the block must be recomputed.
   auto body = [&](const uint32_t qblk, auto fastc) __attribute__((always_inline)) -> bool {
   constexpr bool FAST = decltype(fastc)::value;
   static_assert(!(FAST && (BIAS || CAUSAL)), "the bias and causal kernels take the SAFE path");
@@ -112,7 +115,6 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   [[maybe_unused]] const uint32_t bvoff =
       BIAS ? (uint32_t)((long long)min(qrow, N - 1) * bias.sq * 4 + 16 * g) : 0u;
   [[maybe_unused]] const float inv_scale = 1.f / scale;
-  [[maybe_unused]] const float inv_scale_log2 = 1.f / scale_log2;
   auto load_bias = [&](f32x4 (&bv)[4 * NH], int key0) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < 4 * NH; ++x)
@@ -238,40 +240,6 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     mx = halves_max(mx);
     if (__builtin_amdgcn_ballot_w64(mx > m_run + grow_thr) != 0) rescale(mx);
   };
-  // FAST path: after a tile's probabilities P = exp2(S c - m_run c) have
-  // been formed and used, a lane whose share of the tile sums past 2^16
-  // sends the wave here.  Each row then moves its reference up by the
-  // exponent e of its largest P (both lanes of a row agree) and the
-  // accumulator and row sum, which already hold this tile, are scaled by
-  // 2^-e -- an exact power of two, so nothing is rounded.  A P that
-  // overflowed, or an accumulator that did (P V past the float range before
-  // the scaling), marks the block for the SAFE recomputation.
-  auto settle = [&](const f32x16 (&p)[NH], float tile_sum) __attribute__((always_inline)) {
-    if (__builtin_amdgcn_ballot_w64(tile_sum > 65536.f) == 0) return;
-    float mx = p[0][0];
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, p[h][i]);
-    mx = halves_max(mx);
-    const uint32_t ex = (__float_as_uint(mx) >> 23) & 0xffu;  // biased exponent (P >= 0)
-    const int e = min(max((int)ex - 127, 0), 126);
-    if (e > 0 && ex != 0xffu) {
-      const float alpha = __uint_as_float((uint32_t)(127 - e) << 23);
-      l_run *= alpha;
-      uint32_t top = 0;  // largest |acc| bit pattern: >= 0x7f800000 means inf or NaN
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          acc[cb][i] *= alpha;
-          top = max(top, __float_as_uint(acc[cb][i]) & 0x7fffffffu);
-        }
-      bad = bad || top >= 0x7f800000u;
-      m_run += (float)e * inv_scale_log2;
-    }
-    bad = bad || ex == 0xffu;
-  };
   auto rowmax_guard = [&](const f32x16 (&s)[NH]) __attribute__((always_inline)) {
     float mx = NH == 2 ? fmaxf(s[0][0], s[NH - 1][0]) : s[0][0];
 #pragma unroll
@@ -279,7 +247,7 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     guard(mx);
   };
   // P = exp(S - m_run) in place; row sum over the float32 P; P in bf16 out.
-  auto exps = [&](f32x16 (&s)[NH], bf16x8 (&p)[2 * NH]) __attribute__((always_inline)) -> float {
+  auto exps = [&](f32x16 (&s)[NH], bf16x8 (&p)[2 * NH]) __attribute__((always_inline)) {
     const float mneg = neg_ref();
     float rs[NH];
 #pragma unroll
@@ -291,14 +259,12 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
 #pragma unroll
       for (int h = 0; h < NH; ++h) rs[h] += s[h][i];
     }
-    const float ts = NH == 2 ? rs[0] + rs[NH - 1] : rs[0];
-    l_run += ts;
+    l_run += NH == 2 ? rs[0] + rs[NH - 1] : rs[0];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       p[2 * h] = to_bf16x8(s[h], 0);
       p[2 * h + 1] = to_bf16x8(s[h], 8);
     }
-    return ts;
   };
 
   // Masked scores: keys past N, and under the causal mask keys after the query.
@@ -477,10 +443,8 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
       extra(k);
       __builtin_amdgcn_sched_barrier(0);
     }
-    const float ts = lsum[0] + lsum[1];
-    l_run += ts;
-    if constexpr (FAST) settle(sc, ts);
-    else guard(fmaxf(mxp[0], mxp[1]));
+    l_run += lsum[0] + lsum[1];
+    if constexpr (!FAST) guard(fmaxf(mxp[0], mxp[1]));
   };
   // This wave's last tile j: no next scores; P_j then O^T += V_j^T P_j^T.
   // Under the causal mask a wave's last tile can come before the workgroup's
@@ -500,9 +464,8 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     barrier_vm<0>();
     if (j + 1 < n_tiles) stage_next(parity, j);  // (causal: tiles past this wave's queries follow)
     bf16x8 p[2 * NH];
-    const float ts = exps(sc_of(parity), p);
+    exps(sc_of(parity), p);
     pv(vtile(parity), p);
-    if constexpr (FAST) settle(sc_of(parity), ts);
   };
   // Steps whose next tile is full, then the rest (masking the next tile's
   // scores is correct for any tile, just slower), then the last tile.
@@ -543,12 +506,22 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   wait_vm<0>();  // no direct load may still be landing when the workgroup ends
 
   const float l_tot = halves_sum(l_run);
-  if constexpr (FAST) bad = bad || (__float_as_uint(l_tot) & 0x7f800000u) == 0x7f800000u;
+  if constexpr (FAST) {
+    uint32_t top = 0;  // largest |acc| bit pattern: >= 0x7f800000 means inf or NaN
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) top = max(top, __float_as_uint(acc[cb][i]) & 0x7fffffffu);
+    bad = bad || !(__float_as_uint(l_tot) < 0x5f800000u) || top >= 0x7f800000u;
+  }
   // (with a bias, a row that saw no finite score has l = 0: O = 0, LSE = -inf)
   const bool empty_row = BIAS && l_tot == 0.f;
   const float inv = empty_row ? 0.f : 1.f / l_tot;
-  if (qrow < N) {
-    uint16_t* Orow = O + head + (size_t)qrow * D;
+  // (the row formed again from the lane id: not held through the scan)
+  const int ln_e = lane_id_here();
+  const int qrow_e = q0 + (ln_e & 31), g_e = ln_e >> 5;
+  if (qrow_e < N) {
+    uint16_t* Orow = O + head + (size_t)qrow_e * D;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -556,9 +529,9 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[cb][4 * q4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(Orow + 32 * cb + 8 * q4 + 4 * g) = v;
+        *reinterpret_cast<bf16x4*>(Orow + 32 * cb + 8 * q4 + 4 * g_e) = v;
       }
-    if (g == 0) LSE[(size_t)bh * N + qrow] = empty_row ? -INFINITY : m_run * scale + __logf(l_tot);
+    if (g_e == 0) LSE[(size_t)bh * N + qrow_e] = empty_row ? -INFINITY : m_run * scale + __logf(l_tot);
   }
   return bad;
   };  // body
