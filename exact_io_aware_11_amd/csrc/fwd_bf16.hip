@@ -73,13 +73,13 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  // set when the FAST path must be redone (zeroed here, before the block's
-  // first barrier)
-  __shared__ int redo[1];
+  // per block (of a causal pair): set when the FAST path must be redone
+  // (zeroed here, before the first barrier)
+  __shared__ int redo[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (tid == 0) redo[0] = 0;
+  if (tid < 2) redo[tid] = 0;
   const int g = lane >> 5, r32 = lane & 31;
   // Causal: a workgroup takes row blocks u and n_qblk - 1 - u, which together
   // visit the same number of key tiles for every u, so all workgroups carry
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
 
-  // FAST (no bias, no causal mask): the reference max is taken on the
+  // FAST (no bias): the reference max is taken on the
   // block's first tile only and kept.  Later probabilities exp(S - m) may
   // exceed 1 by anything float32 holds, which costs no relative precision,
   // and need no per-tile max.  A block whose row sum ends at 2^64 or beyond
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   // whether the block must be recomputed.
   auto body = [&](const uint32_t qblk, auto fastc) __attribute__((always_inline)) -> bool {
   constexpr bool FAST = decltype(fastc)::value;
-  static_assert(!(FAST && (BIAS || CAUSAL)), "the bias and causal kernels take the SAFE path");
+  static_assert(!(FAST && BIAS), "the bias kernels take the SAFE path");
   bool bad = false;
   const int q0 = (int)qblk * BM + wave * 32;  // first query row of this wave
   const int qrow = q0 + r32;                  // the query of this lane's column
@@ -536,14 +536,26 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   return bad;
   };  // body
 
-  // With a bias, and under the causal mask, the SAFE path alone: on causal
-  // blocks the FAST path measured 2 % slower at N = 4096 and no faster at
-  // N = 8192, on full rows 2-3 % faster.  Otherwise the FAST path, and if any
-  // lane of the workgroup reports a non-finite row sum or accumulator, the
-  // SAFE path again on the same block (it overwrites the block's outputs).
+  // Without a bias: the FAST path, and if any lane of the workgroup reports a
+  // row sum or accumulator out of range, the SAFE path again on the same
+  // block (it overwrites the block's outputs); causal: for each block of the
+  // pair, with its own flag.  With a bias: the SAFE path alone.
   using FASTC = std::true_type;
   using SAFEC = std::false_type;
-  if constexpr (CAUSAL) {
+  if constexpr (CAUSAL && !BIAS) {
+    auto one = [&](uint32_t qb, int slot) __attribute__((always_inline)) {
+      const bool bad = body(qb, FASTC{});
+      if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo[slot] = 1;
+      barrier_vm<0>();
+      if (redo[slot] != 0) {
+        body(qb, SAFEC{});
+        barrier_vm<0>();
+      }
+    };
+    const uint32_t partner = n_qblk - 1 - unit;
+    one(partner, 0);  // the longer block first
+    if (partner != unit) one(unit, 1);  // (uniform over the workgroup)
+  } else if constexpr (CAUSAL) {
     const uint32_t partner = n_qblk - 1 - unit;
     body(partner, SAFEC{});  // the longer block first
     if (partner != unit) {  // uniform over the workgroup
