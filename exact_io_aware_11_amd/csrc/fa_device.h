@@ -77,8 +77,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
 }
 // The same for a tile of `rows` rows of ROW_BYTES bytes (rows may be <= 0),
 // saturated in 32-bit arithmetic: rows past the largest count that fits
-// 2^32 - 1 bytes give 2^32 - 1.  (The 64-bit form of make_rsrc moved the
-// register allocation of the dQ kernel with a bias into heavy spilling.)
+// 2^32 - 1 bytes give 2^32 - 1.  The 64-bit form above needs a vector
+// compare per call (gfx950 has no unsigned 64-bit scalar compare), which in
+// the tile loops costs instructions and, in the dQ kernel with a bias, pushed
+// the register allocation into heavy spilling.
 template <int ROW_BYTES>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_tile_rsrc(const void* base, int rows) {
   constexpr int kMaxRows = (int)(0xFFFFFFFFu / ROW_BYTES);

@@ -173,7 +173,7 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   // ends at the head's end: rows past N arrive as zeros (those keys are
   // masked, so their scores never count and their P is exactly 0).
   auto tile_rsrc = [&](const uint16_t* src, int key0) __attribute__((always_inline)) {
-    return make_rsrc(src + (size_t)key0 * D, (long)(N - key0) * (2 * D));
+    return make_tile_rsrc<2 * D>(src + (size_t)key0 * D, N - key0);
   };
   auto stage = [&](const uint16_t* src, uint16_t* dst, int key0) __attribute__((always_inline)) {
     const auto r = tile_rsrc(src, key0);

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(
     ldoff[x] = (uint32_t)(row * 2 * D + ((((byte % (2 * D)) >> 4) ^ swz<D>(row)) << 4));
   }
   auto stage = [&](const uint16_t* src, uint16_t* dst, int key0) __attribute__((always_inline)) {
-    const auto r = make_rsrc(src + (size_t)key0 * D, (long)(N - key0) * (2 * D));
+    const auto r = make_tile_rsrc<2 * D>(src + (size_t)key0 * D, N - key0);
 #pragma unroll
     for (int x = 0; x < LPW; ++x) load_lds16(r, dst + (wave * LPW + x) * 512, ldoff[x]);
   };

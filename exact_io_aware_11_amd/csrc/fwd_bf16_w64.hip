@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(
     ldoff[x] = (uint32_t)(row * 2 * D + ((((byte % (2 * D)) >> 4) ^ swz<D>(row)) << 4));
   }
   auto tile_rsrc = [&](const uint16_t* src, int key0) __attribute__((always_inline)) {
-    return make_rsrc(src + (size_t)key0 * D, (long)(N - key0) * (2 * D));
+    return make_tile_rsrc<2 * D>(src + (size_t)key0 * D, N - key0);
   };
   // This wave's share of K tile jk and V tile jv into their ring slots (K
   // first, then V: the order the barrier counts on).

@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     ldoff[x] = (uint32_t)(row * D + 16 * (((byte % D) >> 4) ^ sw8<D>(row)));
   }
   auto tile_rsrc = [&](const uint8_t* src, int key0) __attribute__((always_inline)) {
-    return make_rsrc(src + (size_t)key0 * D, (long)(N - key0) * D);
+    return make_tile_rsrc<D>(src + (size_t)key0 * D, N - key0);
   };
   auto stage = [&](const uint8_t* src, uint8_t* dst, int key0) __attribute__((always_inline)) {
     const auto r = tile_rsrc(src, key0);
@@ -208,10 +208,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   // tile past the end arrives as zeros (unused).
   const int nkb = (N + 31) / 32;
   auto kscale_rsrc = [&](int key0) __attribute__((always_inline)) {
-    return make_rsrc(KS + ((size_t)bh * N + key0) * 4, (long)(N - key0) * 4);
+    return make_tile_rsrc<4>(KS + ((size_t)bh * N + key0) * 4, N - key0);
   };
   auto vscale_rsrc = [&](int key0) __attribute__((always_inline)) {
-    return make_rsrc(VS + ((size_t)bh * nkb + key0 / 32) * D, (long)(nkb - key0 / 32) * D);
+    return make_tile_rsrc<D>(VS + ((size_t)bh * nkb + key0 / 32) * D, nkb - key0 / 32);
   };
   auto stage_kscale = [&](uint8_t* dst, int key0) __attribute__((always_inline)) {
     if constexpr (MX) {
