@@ -27,6 +27,14 @@
 //  * K and V tiles are double-buffered in LDS (16-byte XOR swizzle), staged
 //    from HBM with 16-byte loads issued one tile ahead; one barrier per tile.
 //  * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA.
+//  * Reference max, two paths.  FAST (no bias): the row max of the block's
+//    first tile, kept for the whole block -- the final division cancels any
+//    reference, so no per-tile max or rescale is needed -- and checked once
+//    at the end: a row sum at 2^64 or beyond, or an accumulator that is not
+//    finite, and the workgroup recomputes the block on the SAFE path.  SAFE
+//    (with a bias, and as that fallback): the running max of the pages, with
+//    a lazy rescale (the reference moves only when a tile exceeds it by
+//    2^16 in probability).
 //  * Optional additive bias (the explainer's V2 section merges mask and bias
 //    into the score stage), -inf masking: a tile's bias (16 bytes of four
 //    consecutive keys per load) is loaded at the start of the step two before
