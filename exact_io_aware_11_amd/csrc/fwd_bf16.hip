@@ -333,7 +333,11 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   // 2 products early in the step, so that it has landed by the next barrier.
   constexpr int DEPTH = D == 64 ? 3 : 4;
   constexpr int NS = NH * (D / 16), NOPS = NS + 2 * NH * (D / 32);  // S products come first
-  constexpr int EXP_OPS = NH == 2 ? NS + 2 * (D / 32) : NS + 2, MAX_OPS = NH == 2 ? 12 : 4;
+  // The mask and row max of S_{j+1} read its finished scores: they ride on
+  // PV products only (at d = 64 that leaves 8 of them).
+  constexpr int EXP_OPS = NH == 2 ? NS + 2 * (D / 32) : NS + 2;
+  constexpr int MAX_OPS = NH == 2 ? (NOPS - NS < 12 ? NOPS - NS : 12) : 4;
+  static_assert(NOPS - MAX_OPS >= NS, "the row max must not see partial scores");
   // the last element of key chunk kc (element 8 kc + 7 of half kc / 2) gets its phase (c), which
   // packs the chunk, in product slot (its phase-(a) slot) + 2, before the chunk's first PV product
   static_assert((7 * EXP_OPS) / (16 * NH) + 2 < NS, "chunk 0 packed before its first PV product");

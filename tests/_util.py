@@ -183,7 +183,10 @@ def bf16_inputs_from(q, k, v, do=None):
 #              before any rescaling
 #  jump_huge_v late keys ~2^40 times it (row sums stay below 2^64), their
 #              values times 2^100: P V overflows while the row sum does not
-OUTGROW_KINDS = ["growing", "jump", "jump_big_v", "jump_huge_v"]
+#  jump_early  as jump from key 100 on: under the causal mask with 256-row
+#              blocks, the short block of a pair (rows 0..255, processed
+#              second) overflows too, not only the long one
+OUTGROW_KINDS = ["growing", "jump", "jump_big_v", "jump_huge_v", "jump_early"]
 
 
 def outgrow_inputs(kind, causal, d, N=700):
@@ -195,9 +198,10 @@ def outgrow_inputs(kind, causal, d, N=700):
         q = np.abs(q) + 0.5
         k = np.abs(k) * np.linspace(0.2, 3.0, N, dtype=np.float32)[None, None, :, None]
     else:
-        big = np.arange(300, N, 97)  # a few late keys, one per row block or so
+        big = np.arange(100 if kind == "jump_early" else 300, N, 97)  # one per row block or so
         q[...] = np.abs(q) + 1.0
-        k[:, :, big, :] = {"jump": 12.0, "jump_big_v": 4.3 if d == 128 else 6.1,
+        k[:, :, big, :] = {"jump": 12.0, "jump_early": 12.0,
+                           "jump_big_v": 4.3 if d == 128 else 6.1,
                            "jump_huge_v": 1.46 if d == 128 else 2.07}[kind]
         if kind == "jump_big_v":
             v[:, :, big, :] *= 2.0 ** 20

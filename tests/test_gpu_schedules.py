@@ -65,3 +65,35 @@ def test_schedule_deterministic_and_agrees_with_default(schedule, causal, monkey
     o_d = float(np.max(np.abs(to_f64(o1) - to_f64(o0))) / np.max(np.abs(to_f64(o0))))
     say(f"{schedule} vs interleaved: LSE {lse_d:.2e}, O {o_d:.2e}")
     assert lse_d <= 1e-5 and o_d <= 2 ** -7
+
+
+@pytest.mark.parametrize("case", ["d64", "bias", "fp8"])
+def test_schedule_applies_to_bf16_d128_without_bias_only(schedule, case, monkeypatch):
+    """Elsewhere (d = 64, a bias, fp8) the variable is accepted and changes
+    nothing: the outputs equal the default's bitwise."""
+    causal = True
+    if case == "d64":
+        inp = fa_inputs.make_inputs((1, 2, 700, 64), "bf16", seed=5, with_dout=False)
+    elif case == "fp8":
+        inp = fa_inputs.make_inputs((1, 2, 700, 128), "fp8", seed=5, with_dout=False)
+    else:
+        inp = fa_inputs.make_inputs((1, 2, 700, 128), "bf16", seed=5, with_dout=False)
+
+    def run():
+        if case != "bias":
+            _, o, lse = run_fwd(inp, 0.1, causal)
+            return o, lse
+        q, k, v = (torch.from_numpy(x).view(torch.int16).view(torch.bfloat16).cuda()
+                   for x in (inp.q, inp.k, inp.v))
+        bias = torch.from_numpy(fa_inputs.draw_bias((1, 1), 700, seed=3, kind="dense")).cuda()
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        fa.fa_fwd_bias(q, k, v, bias[..., :700], o, lse, 0.1, causal)
+        torch.cuda.synchronize()
+        return o, lse
+
+    o1, l1 = run()
+    monkeypatch.setenv("FA_FWD_SCHEDULE", "interleaved")
+    o0, l0 = run()
+    assert torch.equal(o1.view(torch.int16), o0.view(torch.int16)) and torch.equal(l1, l0)
+
