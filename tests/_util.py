@@ -190,6 +190,11 @@ OUTGROW_KINDS = ["growing", "jump", "jump_big_v", "jump_huge_v", "jump_early"]
 
 
 def outgrow_inputs(kind, causal, d, N=700):
+    return bf16_inputs_from(*outgrow_f32(kind, causal, d, N))
+
+
+def outgrow_f32(kind, causal, d, N=700):
+    """The float32 Q, K, V, dO behind outgrow_inputs."""
     rng = np.random.default_rng(31 + d + int(causal))
     q = rng.standard_normal((1, 2, N, d)).astype(np.float32)
     k = rng.standard_normal((1, 2, N, d)).astype(np.float32)
@@ -208,7 +213,7 @@ def outgrow_inputs(kind, causal, d, N=700):
         if kind == "jump_huge_v":
             v[:, :, big, :] *= 2.0 ** 100
     do = rng.standard_normal((1, 2, N, d)).astype(np.float32)
-    return bf16_inputs_from(q, k, v, do)
+    return q, k, v, do
 
 
 def sampled_fwd_check(w, heads, rows, seed=42, block=256):

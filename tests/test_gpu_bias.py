@@ -102,6 +102,23 @@ def test_bf16_dense_bias(N, d, causal):
                f"bf16 dense bias 2x3x{N}x{d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("at", [5, 100, 400])
+def test_bf16_bias_that_jumps(at, causal, d):
+    """A bias column of +200 at one key (and +150 on a later one): every row
+    that sees it has its maximum there, far above the scores of its first
+    tile, so the reference max must move before those probabilities are
+    formed (the SAFE path's lazy rescale); at key 5 the jump lies in the
+    first tile itself."""
+    N = 700
+    inp = fa_inputs.make_inputs((1, 2, N, d), "bf16", seed=at + d)
+    b = fa_inputs.draw_bias((1, 2), N, seed=at, kind="dense", p_mask=0.0)
+    b[..., :, at] = 200.0
+    b[..., :, min(at + 333, N - 1)] = 150.0
+    check_case(inp, b, 1 / math.sqrt(d), causal, f"bf16 jumping bias at {at} d={d}")
+
+
 @pytest.mark.parametrize("N", [31, 32, 33, 63, 64, 96, 97, 129])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_bias_tile_boundaries(N, causal):

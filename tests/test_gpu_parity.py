@@ -15,8 +15,8 @@ import pytest
 import fa_inputs
 import oracle
 from _util import (OUTGROW_KINDS, bf16_inputs_from, check, exact_values, full_check_fwd,
-                   outgrow_inputs, rows_by_key_chunks, run_bwd, run_fwd, sample_rows,
-                   sampled_fwd_check, say, to_f64)
+                   outgrow_f32, outgrow_inputs, rows_by_key_chunks, run_bwd, run_fwd,
+                   sample_rows, sampled_fwd_check, say, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -174,6 +174,44 @@ def test_scores_that_outgrow_the_first_tile(kind, causal, d):
     oracle)."""
     full_check_fwd(outgrow_inputs(kind, causal, d), 1 / math.sqrt(d), causal,
                    f"bf16 {kind} d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["growing", "jump", "jump_early"])
+def test_backward_of_scores_that_outgrow_the_first_tile(kind, causal, d):
+    """The backward recomputes P from the saved LSE, so a row's far larger
+    late scores need no rescale there; forward and backward against the
+    oracle on the same inputs.  With the jumping keys every row's mass sits
+    on keys that share one K row, so the exact dQ = scale sum_j dS_ij K_j
+    cancels to ~0 (sum_j dS_ij = 0); the bf16 dS of any implementation leaves
+    a rounding residue there that no relative bar can hold, so for those
+    cases dQ is checked for finiteness only, dK and dV against the oracle."""
+    inp = outgrow_inputs(kind, causal, d)
+    scale = 1 / math.sqrt(d)
+    if kind == "growing":
+        full_check_bwd(inp, scale, causal, f"bf16 bwd {kind} d={d}")
+        return
+    dev, o, lse, (qs, ks, vs) = full_check_fwd(inp, scale, causal, f"bf16 bwd {kind} d={d}")
+    (dq, dk, dv), _ = run_bwd(dev, o, lse, inp, scale, causal)
+    _, rk, rv = oracle.attn_bwd(qs, ks, vs, exact_values(inp.dout, "bf16"), scale, causal)
+    assert np.isfinite(to_f64(dq)).all()
+    check(f"bf16 bwd {kind} d={d} dK", to_f64(dk), rk, "bf16")
+    check(f"bf16 bwd {kind} d={d} dV", to_f64(dv), rv, "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["growing", "jump", "jump_early"])
+def test_fp8_scores_that_outgrow_the_first_tile(kind, causal, d):
+    """The fp8 forward keeps its reference within a factor 1.75 of the row
+    max (2^8 P must stay below 448): late scores far above the first tile's
+    move it.  The inputs are quantised per tensor, so the jumping keys set
+    K's scale and the other keys keep only a few code steps."""
+    q, k, v, _ = outgrow_f32(kind, causal, d)
+    (cq, sq), (ck, sk), (cv, sv) = (fa_inputs.quantize_e4m3fn(t) for t in (q, k, v))
+    inp = fa_inputs.Inputs(cq, ck, cv, None, (sq, sk, sv), "fp8")
+    full_check_fwd(inp, 1 / math.sqrt(d), causal, f"fp8 {kind} d={d}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
