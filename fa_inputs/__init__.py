@@ -162,9 +162,13 @@ def draw_spread_f32(shape, seed: int = 42, spread_log2: float = 0.0):
 
 
 def make_mx_inputs(shape, seed: int = 42, spread_log2: float = 0.0) -> MXInputs:
-    """draw_spread_f32's Q, K, V, block-quantized: Q and K in blocks along the
-    head dim, V in blocks along the sequence."""
-    q, k, v = draw_spread_f32(shape, seed, spread_log2)
+    """draw_spread_f32's Q, K, V, block-quantized (mx_inputs_from)."""
+    return mx_inputs_from(*draw_spread_f32(shape, seed, spread_log2))
+
+
+def mx_inputs_from(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> MXInputs:
+    """float32 Q, K, V block-quantized: Q and K in blocks along the head dim,
+    V in blocks along the sequence."""
     (qc, qs), (kc, ks) = quantize_mx_e4m3fn(q, -1), quantize_mx_e4m3fn(k, -1)
     vc, vs = quantize_mx_e4m3fn(v, -2)
 

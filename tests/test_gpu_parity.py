@@ -214,6 +214,31 @@ def test_fp8_scores_that_outgrow_the_first_tile(kind, causal, d):
     full_check_fwd(inp, 1 / math.sqrt(d), causal, f"fp8 {kind} d={d}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["growing", "jump", "jump_early", "jump_huge_v"])
+def test_fp32_scores_that_outgrow_the_first_tile(kind, causal):
+    """The float32 kernels' online softmax on the same inputs (d = 64, the
+    float32 head size).  The float32 bar of 1e-5 is for N(0,1) inputs; here
+    scaled scores reach S_max = 30..170, and exp(s - m) carries the float32
+    rounding of s - m, about S_max 2^-24 relative.  Bar, relative to the
+    output scale and for the LSE absolute: 1e-5 + 2^-21 S_max (8 roundings
+    of the largest score)."""
+    q, k, v, do = outgrow_f32(kind, causal, 64)
+    scale = 1 / 8
+    s_max = float(np.max(np.abs(np.einsum("bhid,bhjd->bhij", q.astype(np.float64),
+                                          k.astype(np.float64))))) * scale
+    bar = 1e-5 + 2.0 ** -21 * s_max
+    inp = fa_inputs.Inputs(q, k, v, do, (1.0, 1.0, 1.0), "fp32")
+    _, o, lse = run_fwd(inp, scale, causal)
+    o_ref, lse_ref = oracle.attn_fwd(q.astype(np.float64), k.astype(np.float64),
+                                     v.astype(np.float64), scale, causal)
+    e_o = float(np.max(np.abs(to_f64(o) - o_ref)) / np.max(np.abs(o_ref)))
+    e_l = float(np.max(np.abs(to_f64(lse) - lse_ref)))
+    say(f"fp32 {kind} causal={causal}: S_max {s_max:.1f}, bar {bar:.2e}, O {e_o:.2e}, "
+        f"LSE {e_l:.2e}")
+    assert np.isfinite(to_f64(o)).all() and e_o <= bar and e_l <= bar
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_runs_are_bitwise_deterministic(dtype):
     inp = fa_inputs.make_inputs((2, 4, 700, 128), dtype, seed=10)
