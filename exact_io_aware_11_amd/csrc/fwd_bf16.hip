@@ -335,7 +335,9 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   constexpr int NS = NH * (D / 16), NOPS = NS + 2 * NH * (D / 32);  // S products come first
   // The mask and row max of S_{j+1} read its finished scores: they ride on
   // PV products only (at d = 64 that leaves 8 of them).
-  constexpr int EXP_OPS = NH == 2 ? NS + 2 * (D / 32) : NS + 2;
+  // (at d = 128 the exp phases spread over 26 of the 32 products, the most
+  // the packing deadline of the last key chunk allows: +0.2-0.6 % over 24)
+  constexpr int EXP_OPS = NH == 2 ? (D == 128 ? NS + 10 : NS + 2 * (D / 32)) : NS + 2;
   constexpr int MAX_OPS = NH == 2 ? (NOPS - NS < 12 ? NOPS - NS : 12) : 4;
   static_assert(NOPS - MAX_OPS >= NS, "the row max must not see partial scores");
   // the last element of key chunk kc (element 8 kc + 7 of half kc / 2) gets its phase (c), which
