@@ -71,6 +71,11 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   __shared__ __attribute__((aligned(1024))) uint16_t lk1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t lv0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t lv1[TILE];
+  // Q rows in and O rows out, 32 rows per wave (each wave uses only its own
+  // rows; same swizzle as the K tiles): both then cross to and from HBM as
+  // whole rows, 16-byte accesses to consecutive addresses, instead of 16
+  // bytes from each of 32 rows per instruction.
+  __shared__ __attribute__((aligned(1024))) uint16_t lq[BM * D];
   auto ktile = [&](auto bufc) -> uint16_t* {
     if constexpr (decltype(bufc)::value == 0) return lk0;
     else return lk1;
@@ -139,12 +144,18 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     for (int h = 0; h < NH; ++h) s[h][i] = bv[4 * h + (i >> 2)][i & 3] * inv_scale;
   };
 
-  // Q fragment as the B operand of S^T = K Q^T: lane holds Q[qrow][16t + 8g .. +7].
-  bf16x8 qf[D / 16];
+  // This wave's Q rows into its LDS rows by direct loads (rows past N arrive
+  // as zeros), issued first; read into registers after the first barrier.
+  // (offsets formed from a fresh lane id: not kept live through the scan)
+  uint16_t* const lqw = lq + wave * 32 * D;
+  {
+    const auto qres = make_tile_rsrc<2 * D>(Qh + (size_t)q0 * D, N - q0);
+    const int ln_q = lane_id_here();
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    if (qrow < N) qf[t] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + 16 * t + 8 * g);
-    else qf[t] = bf16x8{};
+    for (int x = 0; x < D / 16; ++x) {
+      const int byte = x * 1024 + 16 * ln_q, row = byte / (2 * D);
+      load_lds16(qres, lqw + x * 512, (uint32_t)(row * 2 * D + ((((byte % (2 * D)) >> 4) ^ swz<D>(row)) << 4)));
+    }
   }
 
   const int kv_end = CAUSAL ? min(N, (int)qblk * BM + BM) : N;
@@ -155,6 +166,9 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   int koff[D / 16];  // K as the A operand: row r32 (+32h), chunk 2t + g
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) koff[t] = tile_off<D>(r32, 2 * t + g);
+  // Q fragment as the B operand of S^T = K Q^T: lane holds Q[qrow][16t + 8g .. +7]
+  // (read from the wave's LDS rows once they have landed).
+  bf16x8 qf[D / 16];
   // V by the transposing read: source lane (r, c) = ((lane%16)/4, lane%4) reads
   // row 4g + r (+8 for keys 8..15 of a 16-key step) at head dim 32cb + 16((lane/16)%2) + 4c.
   const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_n0 = 16 * ((lane >> 4) & 1);
@@ -309,6 +323,11 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   stage(Kh, lk0, 0);
   stage(Vh, lv0, 0);
   barrier_vm<0>();
+  {
+    const int ln_r = lane_id_here();
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) qf[t] = lds_read_b128(lqw + tile_off<D>(ln_r & 31, 2 * t + (ln_r >> 5)));
+  }
   stage(Kh, lk1, BN);  // (a tile past the end arrives as zeros; never used)
   scores(lk0, sa);
   if constexpr (BIAS) {
@@ -533,20 +552,27 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   const float inv = empty_row ? 0.f : 1.f / l_tot;
   // (the row formed again from the lane id: not held through the scan)
   const int ln_e = lane_id_here();
-  const int qrow_e = q0 + (ln_e & 31), g_e = ln_e >> 5;
-  if (qrow_e < N) {
-    uint16_t* Orow = O + head + (size_t)qrow_e * D;
+  const int r_e = ln_e & 31, g_e = ln_e >> 5, qrow_e = q0 + r_e;
+  // O through the wave's LDS rows: the lane's four runs of 4 head dims per 32
+  // go in as 8-byte writes, whole rows come back as 16-byte reads and leave
+  // as stores of 4 consecutive rows (1 KiB) per instruction.
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+  for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 v;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[cb][4 * q4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(Orow + 32 * cb + 8 * q4 + 4 * g_e) = v;
-      }
-    if (g_e == 0) LSE[(size_t)bh * N + qrow_e] = empty_row ? -INFINITY : m_run * scale + __logf(l_tot);
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[cb][4 * q4 + e] * inv);
+      *reinterpret_cast<bf16x4*>(lqw + tile_off<D>(r_e, 4 * cb + q4) + 4 * g_e) = v;
+    }
+#pragma unroll
+  for (int x = 0; x < D / 16; ++x) {
+    const int byte = x * 1024 + 16 * ln_e, row = byte / (2 * D), chunk = (byte % (2 * D)) >> 4;
+    const bf16x8 w = lds_read_b128(lqw + tile_off<D>(row, chunk));
+    if (q0 + row < N) *reinterpret_cast<bf16x8*>(O + head + (size_t)(q0 + row) * D + 8 * chunk) = w;
   }
+  if (g_e == 0 && qrow_e < N)
+    LSE[(size_t)bh * N + qrow_e] = empty_row ? -INFINITY : m_run * scale + __logf(l_tot);
   return bad;
   };  // body
 
@@ -560,10 +586,10 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     auto one = [&](uint32_t qb, int slot) __attribute__((always_inline)) {
       const bool bad = body(qb, FASTC{});
       if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo[slot] = 1;
-      barrier_vm<0>();
+      barrier_vm<63>();  // (the block's O stores may still be in flight)
       if (redo[slot] != 0) {
         body(qb, SAFEC{});
-        barrier_vm<0>();
+        barrier_vm<63>();
       }
     };
     const uint32_t partner = n_qblk - 1 - unit;
@@ -573,7 +599,7 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     const uint32_t partner = n_qblk - 1 - unit;
     body(partner, SAFEC{});  // the longer block first
     if (partner != unit) {  // uniform over the workgroup
-      barrier_vm<0>();  // every wave is done with the first block's LDS tiles
+      barrier_vm<63>();  // every wave is done with the first block's LDS tiles
       body(unit, SAFEC{});
     }
   } else if constexpr (BIAS) {
@@ -581,7 +607,7 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   } else {
     const bool bad = body(unit, FASTC{});
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo[0] = 1;
-    barrier_vm<0>();  // (also: every wave is done with the LDS tiles)
+    barrier_vm<63>();  // (also: every wave is done with the LDS tiles)
     if (redo[0] != 0)  // uniform over the workgroup
       body(unit, SAFEC{});
   }
