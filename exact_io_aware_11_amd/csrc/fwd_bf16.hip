@@ -43,12 +43,17 @@
 //    scale, the starting value of the score accumulators.  Only one tile's
 //    bias is held at a time.  A row that sees no finite score ends with O = 0
 //    and LSE = -inf.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
+
+// Blocks one workgroup may take (its FAST-path flags live in LDS).
+constexpr int kFwdMaxSeq = 256;
 
 // Two waves per SIMD (64 KiB of LDS per workgroup and at most 256 registers
 // per wave: two workgroups of 4 waves or one of 8 per CU); at d = 64 without
@@ -86,24 +91,47 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  // per block (of a causal pair): set when the FAST path must be redone
-  // (zeroed here, before the first barrier)
-  __shared__ int redo[2];
+  // per block of this workgroup, in order: set when the FAST path must be
+  // redone (zeroed here, before the first barrier)
+  __shared__ int redo[kFwdMaxSeq];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (tid < 2) redo[tid] = 0;
+  for (int i = tid; i < kFwdMaxSeq; i += 64 * WAVES) redo[i] = 0;
   const int g = lane >> 5, r32 = lane & 31;
   // Causal: a workgroup takes row blocks u and n_qblk - 1 - u, which together
   // visit the same number of key tiles for every u, so all workgroups carry
   // equal work and each pays its set-up once per two blocks.
   const uint32_t n_units = CAUSAL ? (n_qblk + 1) / 2 : n_qblk;
-  uint32_t bh, unit;
-  map_block(blockIdx.x, n_units, total, kOrderPlain, bh, unit);
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
+  // The (batch, head) of the current unit (a workgroup takes units blockIdx.x,
+  // blockIdx.x + gridDim.x, ...).
+  uint32_t bh = 0;
+  size_t head = 0;
+  const uint16_t *Qh = Q, *Kh = K, *Vh = V;
+  uint16_t* const lqw = lq + wave * 32 * D;  // this wave's Q / O rows
+
+  // A block's first loads, issued ahead of the block: this wave's Q rows into
+  // its LDS rows (rows past N arrive as zeros) and its share of K_0 and V_0
+  // into tile buffers 0.  (Offsets formed from a fresh lane id: nothing here
+  // stays live through a scan.)
+  auto row_off = [](uint32_t byte) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t row = byte / (2 * D);  // byte offset in global of the chunk the swizzle puts at `byte`
+    return row * 2 * D + ((((byte % (2 * D)) >> 4) ^ (uint32_t)swz<D>((int)row)) << 4);
+  };
+  auto issue = [&](const uint32_t qblk) __attribute__((always_inline)) {
+    const int q0 = (int)qblk * BM + wave * 32;
+    const uint32_t ln = (uint32_t)lane_id_here();
+    const auto qres = make_tile_rsrc<2 * D>(Qh + (size_t)q0 * D, N - q0);
+#pragma unroll
+    for (int x = 0; x < D / 16; ++x) load_lds16(qres, lqw + x * 512, row_off(x * 1024u + 16u * ln));
+    const auto kres = make_tile_rsrc<2 * D>(Kh, N), vres = make_tile_rsrc<2 * D>(Vh, N);
+#pragma unroll
+    for (int x = 0; x < LPW; ++x) {
+      const uint32_t o = row_off((uint32_t)(wave * LPW + x) * 1024u + 16u * ln);
+      load_lds16(kres, lk0 + (wave * LPW + x) * 512, o);
+      load_lds16(vres, lv0 + (wave * LPW + x) * 512, o);
+    }
+  };
 
   // FAST (no bias): the reference max is taken on the
   // block's first tile only and kept.  Later probabilities exp(S - m) may
@@ -144,19 +172,6 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     for (int h = 0; h < NH; ++h) s[h][i] = bv[4 * h + (i >> 2)][i & 3] * inv_scale;
   };
 
-  // This wave's Q rows into its LDS rows by direct loads (rows past N arrive
-  // as zeros), issued first; read into registers after the first barrier.
-  // (offsets formed from a fresh lane id: not kept live through the scan)
-  uint16_t* const lqw = lq + wave * 32 * D;
-  {
-    const auto qres = make_tile_rsrc<2 * D>(Qh + (size_t)q0 * D, N - q0);
-    const int ln_q = lane_id_here();
-#pragma unroll
-    for (int x = 0; x < D / 16; ++x) {
-      const int byte = x * 1024 + 16 * ln_q, row = byte / (2 * D);
-      load_lds16(qres, lqw + x * 512, (uint32_t)(row * 2 * D + ((((byte % (2 * D)) >> 4) ^ swz<D>(row)) << 4)));
-    }
-  }
 
   const int kv_end = CAUSAL ? min(N, (int)qblk * BM + BM) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
@@ -320,9 +335,7 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     load_bias(bv0, 0);
     load_bias(bv, BN);
   }
-  stage(Kh, lk0, 0);
-  stage(Vh, lv0, 0);
-  barrier_vm<0>();
+  barrier_vm<0>();  // the block's Q rows, K_0 and V_0 (issue()) have landed
   {
     const int ln_r = lane_id_here();
 #pragma unroll
@@ -576,41 +589,84 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   return bad;
   };  // body
 
-  // Without a bias: the FAST path, and if any lane of the workgroup reports a
-  // row sum or accumulator out of range, the SAFE path again on the same
-  // block (it overwrites the block's outputs); causal: for each block of the
-  // pair, with its own flag.  With a bias: the SAFE path alone.
-  using FASTC = std::true_type;
+  // The workgroup's blocks run back to back: unit after unit, and under the
+  // causal mask the pair's longer block first.  Each block's first loads are
+  // issued as soon as this wave has stored the previous block's O: tile
+  // buffers 0 are free then when the previous block ended on an odd tile
+  // index (its last tile in buffers 1, which the other waves may still read);
+  // otherwise every wave first meets at a barrier.  Without a bias every
+  // block takes the FAST path and records in redo[] whether any lane of the
+  // workgroup found it out of range; those blocks are computed again on the
+  // SAFE path after the last one (overwriting their outputs).  With a bias:
+  // the SAFE path.
+  using RUNC = std::integral_constant<bool, !BIAS>;
   using SAFEC = std::false_type;
-  if constexpr (CAUSAL && !BIAS) {
-    auto one = [&](uint32_t qb, int slot) __attribute__((always_inline)) {
-      const bool bad = body(qb, FASTC{});
-      if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo[slot] = 1;
-      barrier_vm<63>();  // (the block's O stores may still be in flight)
-      if (redo[slot] != 0) {
-        body(qb, SAFEC{});
-        barrier_vm<63>();
-      }
-    };
-    const uint32_t partner = n_qblk - 1 - unit;
-    one(partner, 0);  // the longer block first
-    if (partner != unit) one(unit, 1);  // (uniform over the workgroup)
-  } else if constexpr (CAUSAL) {
-    const uint32_t partner = n_qblk - 1 - unit;
-    body(partner, SAFEC{});  // the longer block first
-    if (partner != unit) {  // uniform over the workgroup
-      barrier_vm<63>();  // every wave is done with the first block's LDS tiles
-      body(unit, SAFEC{});
+  auto tiles_of = [&](uint32_t qb) __attribute__((always_inline)) {
+    const int kv_end = CAUSAL ? min(N, (int)qb * BM + BM) : N;
+    return (kv_end + BN - 1) / BN;
+  };
+  auto set_unit = [&](uint32_t vb) __attribute__((always_inline)) -> uint32_t {
+    uint32_t unit;
+    map_block(vb, n_units, total, kOrderPlain, bh, unit);
+    head = (size_t)bh * (size_t)N * D;
+    Qh = Q + head;
+    Kh = K + head;
+    Vh = V + head;
+    return unit;
+  };
+  int seq = 0;
+  bool free0 = true;  // (uniform) no wave reads tile buffers 0 any more
+  auto block = [&](uint32_t qb) __attribute__((always_inline)) {
+    if (!free0) barrier_vm<63>();
+    issue(qb);
+    const bool bad = body(qb, RUNC{});
+    if constexpr (!BIAS)
+      if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo[seq] = 1;
+    free0 = (tiles_of(qb) & 1) == 0;
+    ++seq;
+  };
+  for (uint32_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
+    const uint32_t unit = set_unit(vb);
+    if constexpr (CAUSAL) {
+      const uint32_t partner = n_qblk - 1 - unit;
+      block(partner);
+      if (partner != unit) block(unit);  // (uniform over the workgroup)
+    } else {
+      block(unit);
     }
-  } else if constexpr (BIAS) {
-    body(unit, SAFEC{});
-  } else {
-    const bool bad = body(unit, FASTC{});
-    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo[0] = 1;
-    barrier_vm<63>();  // (also: every wave is done with the LDS tiles)
-    if (redo[0] != 0)  // uniform over the workgroup
-      body(unit, SAFEC{});
   }
+  if constexpr (!BIAS) {
+    barrier_vm<63>();  // every flag is written, every tile read
+    int s = 0;
+    for (uint32_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
+      const uint32_t unit = set_unit(vb);
+      const uint32_t partner = CAUSAL ? n_qblk - 1 - unit : unit;
+      for (int k = 0; k < (CAUSAL && partner != unit ? 2 : 1); ++k, ++s) {
+        if (__builtin_amdgcn_readfirstlane(redo[s]) != 0) {
+          const uint32_t qb = k == 0 ? partner : unit;
+          issue(qb);
+          body(qb, SAFEC{});
+          barrier_vm<63>();
+        }
+      }
+    }
+  }
+}
+
+// Compute units of the current device (looked up once per device).
+static int cu_count() {
+  static std::atomic<int> known[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < 64) {
+    const int n = known[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+  }
+  int n = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0 && dev < 64) known[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 template <int D, bool CAUSAL, int WAVES, bool BIAS>
@@ -619,7 +675,15 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   const uint32_t n_qblk = (uint32_t)((a.N + BM - 1) / BM);
   const uint32_t n_units = CAUSAL ? (n_qblk + 1) / 2 : n_qblk;  // row blocks paired when causal
   const uint32_t total = (uint32_t)(a.BH * n_units);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WAVES, BIAS>), dim3(total), dim3(64 * WAVES), 0,
+  // As many workgroups as the CUs hold at once (one of 8 waves, two of 4
+  // with a bias, three at d = 64), each taking units blockIdx.x + k gridDim.x
+  // back to back -- but never more than kFwdMaxSeq blocks per workgroup.
+  constexpr int kPerCu = D == 64 && !BIAS ? 3 : 8 / WAVES;
+  const uint64_t per = CAUSAL ? 2 : 1;
+  const uint64_t slots = (uint64_t)cu_count() * kPerCu;
+  const uint64_t least = ((uint64_t)total * per + kFwdMaxSeq - 1) / kFwdMaxSeq;
+  const uint32_t grid = (uint32_t)std::min<uint64_t>(total, std::max(slots, least));
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WAVES, BIAS>), dim3(grid), dim3(64 * WAVES), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, n_qblk, total, a.scale, a.scale * kLog2e,
                      kRescaleLog2 / (a.scale * kLog2e), a.bias);
