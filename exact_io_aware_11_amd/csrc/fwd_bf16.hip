@@ -76,10 +76,9 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   __shared__ __attribute__((aligned(1024))) uint16_t lk1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t lv0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t lv1[TILE];
-  // Q rows in and O rows out, 32 rows per wave (each wave uses only its own
-  // rows; same swizzle as the K tiles): both then cross to and from HBM as
-  // whole rows, 16-byte accesses to consecutive addresses, instead of 16
-  // bytes from each of 32 rows per instruction.
+  // Q rows, 32 per wave (each wave uses only its own; same swizzle as the K
+  // tiles): they arrive from HBM as whole rows, 16-byte loads of consecutive
+  // addresses, instead of 16 bytes from each of 32 rows per instruction.
   __shared__ __attribute__((aligned(1024))) uint16_t lq[BM * D];
   auto ktile = [&](auto bufc) -> uint16_t* {
     if constexpr (decltype(bufc)::value == 0) return lk0;
@@ -107,7 +106,7 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   // blockIdx.x + gridDim.x, ...).
   uint32_t bh = 0;
   size_t head = 0;
-  const uint16_t *Qh = Q, *Kh = K, *Vh = V;
+  const uint16_t *Kh = K, *Vh = V;
   uint16_t* const lqw = lq + wave * 32 * D;  // this wave's Q / O rows
 
   // A block's first loads, issued ahead of the block: this wave's Q rows into
@@ -118,19 +117,34 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     const uint32_t row = byte / (2 * D);  // byte offset in global of the chunk the swizzle puts at `byte`
     return row * 2 * D + ((((byte % (2 * D)) >> 4) ^ (uint32_t)swz<D>((int)row)) << 4);
   };
-  auto issue = [&](const uint32_t qblk) __attribute__((always_inline)) {
+  auto issue_q = [&](const uint16_t* Qhead, const uint32_t qblk) __attribute__((always_inline)) {
     const int q0 = (int)qblk * BM + wave * 32;
     const uint32_t ln = (uint32_t)lane_id_here();
-    const auto qres = make_tile_rsrc<2 * D>(Qh + (size_t)q0 * D, N - q0);
+    const auto qres = make_tile_rsrc<2 * D>(Qhead + (size_t)q0 * D, N - q0);
 #pragma unroll
     for (int x = 0; x < D / 16; ++x) load_lds16(qres, lqw + x * 512, row_off(x * 1024u + 16u * ln));
-    const auto kres = make_tile_rsrc<2 * D>(Kh, N), vres = make_tile_rsrc<2 * D>(Vh, N);
+  };
+  auto issue_kv = [&](const uint16_t* Khead, const uint16_t* Vhead) __attribute__((always_inline)) {
+    const uint32_t ln = (uint32_t)lane_id_here();
+    const auto kres = make_tile_rsrc<2 * D>(Khead, N), vres = make_tile_rsrc<2 * D>(Vhead, N);
 #pragma unroll
     for (int x = 0; x < LPW; ++x) {
       const uint32_t o = row_off((uint32_t)(wave * LPW + x) * 1024u + 16u * ln);
       load_lds16(kres, lk0 + (wave * LPW + x) * 512, o);
       load_lds16(vres, lv0 + (wave * LPW + x) * 512, o);
     }
+  };
+  // The next block's first loads, issued by each wave right after the current
+  // block's last barrier (set by the caller before each block): its Q rows
+  // (the Q rows of this block are in registers by then), and its K_0 and V_0
+  // when tile buffers 0 are free -- the current block's last tile is in
+  // buffers 1 (an even number of tiles), which the other waves may still read.
+  bool pf_q = false, pf_kv = false;
+  uint32_t pf_qb = 0;
+  const uint16_t *pf_Qh = Q, *pf_Kh = K, *pf_Vh = V;
+  auto on_last = [&]() __attribute__((always_inline)) {
+    if (pf_q) issue_q(pf_Qh, pf_qb);
+    if (pf_kv) issue_kv(pf_Kh, pf_Vh);
   };
 
   // FAST (no bias): the reference max is taken on the
@@ -509,6 +523,7 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   auto step_last = [&](auto parity, int j) __attribute__((always_inline)) {
     barrier_vm<0>();
     if (j + 1 < n_tiles) stage_next(parity, j);  // (causal: tiles past this wave's queries follow)
+    else on_last();
     bf16x8 p[2 * NH];
     exps(sc_of(parity), p);
     pv(vtile(parity), p);
@@ -546,10 +561,13 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
       if (j + 1 < n_tiles) {
         if (j & 1) stage_next(B1{}, j);
         else stage_next(B0{}, j);
+      } else {
+        on_last();
       }
     }
   }
-  wait_vm<0>();  // no direct load may still be landing when the workgroup ends
+  // (every tile load of this block has landed: each wave waited for its own
+  // before the last barrier; only the next block's loads may be in flight)
 
   const float l_tot = halves_sum(l_run);
   if constexpr (FAST) {
@@ -566,23 +584,27 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   // (the row formed again from the lane id: not held through the scan)
   const int ln_e = lane_id_here();
   const int r_e = ln_e & 31, g_e = ln_e >> 5, qrow_e = q0 + r_e;
-  // O through the wave's LDS rows: the lane's four runs of 4 head dims per 32
-  // go in as 8-byte writes, whole rows come back as 16-byte reads and leave
-  // as stores of 4 consecutive rows (1 KiB) per instruction.
+  // O through 2 KiB of LDS per wave in K tile buffer 1 (free during the last
+  // tile, whatever its parity), 32 head dims at a time: the lane's four runs
+  // of 4 dims go in as 8-byte writes ([32 rows][64 bytes], 16-byte chunks
+  // XOR-swizzled by row / 4), and leave as 16-byte reads of 16 rows x 64
+  // bytes per instruction, stored as 64 contiguous bytes per row.
+  uint16_t* const low = lk1 + wave * 1024;
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb)
+  for (int cb = 0; cb < D / 32; ++cb) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       bf16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[cb][4 * q4 + e] * inv);
-      *reinterpret_cast<bf16x4*>(lqw + tile_off<D>(r_e, 4 * cb + q4) + 4 * g_e) = v;
+      *reinterpret_cast<bf16x4*>(low + r_e * 32 + ((q4 ^ ((r_e >> 2) & 3)) << 3) + 4 * g_e) = v;
     }
 #pragma unroll
-  for (int x = 0; x < D / 16; ++x) {
-    const int byte = x * 1024 + 16 * ln_e, row = byte / (2 * D), chunk = (byte % (2 * D)) >> 4;
-    const bf16x8 w = lds_read_b128(lqw + tile_off<D>(row, chunk));
-    if (q0 + row < N) *reinterpret_cast<bf16x8*>(O + head + (size_t)(q0 + row) * D + 8 * chunk) = w;
+    for (int x = 0; x < 2; ++x) {
+      const int row = 16 * x + (ln_e >> 2), c = ln_e & 3;
+      const bf16x8 w = lds_read_b128(low + row * 32 + ((c ^ ((row >> 2) & 3)) << 3));
+      if (q0 + row < N) *reinterpret_cast<bf16x8*>(O + head + (size_t)(q0 + row) * D + 32 * cb + 8 * c) = w;
+    }
   }
   if (g_e == 0 && qrow_e < N)
     LSE[(size_t)bh * N + qrow_e] = empty_row ? -INFINITY : m_run * scale + __logf(l_tot);
@@ -590,11 +612,10 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   };  // body
 
   // The workgroup's blocks run back to back: unit after unit, and under the
-  // causal mask the pair's longer block first.  Each block's first loads are
-  // issued as soon as this wave has stored the previous block's O: tile
-  // buffers 0 are free then when the previous block ended on an odd tile
-  // index (its last tile in buffers 1, which the other waves may still read);
-  // otherwise every wave first meets at a barrier.  Without a bias every
+  // causal mask the pair's longer block first.  Each wave issues the next
+  // block's Q rows (and, when tile buffers 0 are free, its K_0 and V_0) at the
+  // current block's last barrier (on_last); otherwise every wave meets at a
+  // barrier after the block and then issues them.  Without a bias every
   // block takes the FAST path and records in redo[] whether any lane of the
   // workgroup found it out of range; those blocks are computed again on the
   // SAFE path after the last one (overwriting their outputs).  With a bias:
@@ -605,49 +626,84 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     const int kv_end = CAUSAL ? min(N, (int)qb * BM + BM) : N;
     return (kv_end + BN - 1) / BN;
   };
-  auto set_unit = [&](uint32_t vb) __attribute__((always_inline)) -> uint32_t {
+  // Block k (0, or 1 for the second block of a causal pair) of unit vb: its
+  // (batch, head) and row block; false past the end or for a pair of one.
+  auto locate = [&](uint32_t vb, int k, uint32_t& bh_o, uint32_t& qb_o) __attribute__((always_inline)) -> bool {
+    if (vb >= total) return false;
     uint32_t unit;
-    map_block(vb, n_units, total, kOrderPlain, bh, unit);
-    head = (size_t)bh * (size_t)N * D;
-    Qh = Q + head;
+    map_block(vb, n_units, total, kOrderPlain, bh_o, unit);
+    const uint32_t partner = CAUSAL ? n_qblk - 1 - unit : unit;
+    qb_o = k == 0 ? partner : unit;
+    return k == 0 || partner != unit;
+  };
+  // the block after (vb, k) in this workgroup's walk
+  auto advance = [&](uint32_t& vb, int& k, uint32_t& bh_o, uint32_t& qb_o) __attribute__((always_inline)) -> bool {
+    if (CAUSAL && k == 0) {
+      k = 1;
+      if (locate(vb, 1, bh_o, qb_o)) return true;
+    }
+    k = 0;
+    vb += gridDim.x;
+    return locate(vb, 0, bh_o, qb_o);
+  };
+  auto set_head = [&](uint32_t b) __attribute__((always_inline)) {
+    bh = b;
+    head = (size_t)b * (size_t)N * D;
     Kh = K + head;
     Vh = V + head;
-    return unit;
   };
-  int seq = 0;
-  bool free0 = true;  // (uniform) no wave reads tile buffers 0 any more
-  auto block = [&](uint32_t qb) __attribute__((always_inline)) {
-    if (!free0) barrier_vm<63>();
-    issue(qb);
-    const bool bad = body(qb, RUNC{});
-    if constexpr (!BIAS)
-      if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo[seq] = 1;
-    free0 = (tiles_of(qb) & 1) == 0;
-    ++seq;
-  };
-  for (uint32_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
-    const uint32_t unit = set_unit(vb);
-    if constexpr (CAUSAL) {
-      const uint32_t partner = n_qblk - 1 - unit;
-      block(partner);
-      if (partner != unit) block(unit);  // (uniform over the workgroup)
-    } else {
-      block(unit);
+  {
+    uint32_t vb = blockIdx.x, cbh = 0, cqb = 0;
+    int k = 0, seq = 0;
+    bool have = locate(vb, 0, cbh, cqb);
+    if (have) {
+      issue_q(Q + (size_t)cbh * (size_t)N * D, cqb);
+      issue_kv(K + (size_t)cbh * (size_t)N * D, V + (size_t)cbh * (size_t)N * D);
+    }
+    while (have) {
+      uint32_t nvb = vb, nbh = 0, nqb = 0;
+      int nk = k;
+      const bool next = advance(nvb, nk, nbh, nqb);
+      const size_t nhead = (size_t)nbh * (size_t)N * D;
+      const bool even = (tiles_of(cqb) & 1) == 0;
+      pf_q = next;
+      pf_kv = next && even;
+      pf_qb = nqb;
+      pf_Qh = Q + nhead;
+      pf_Kh = K + nhead;
+      pf_Vh = V + nhead;
+      set_head(cbh);
+      const bool bad = body(cqb, RUNC{});
+      if constexpr (!BIAS)
+        if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo[seq] = 1;
+      if (next && !even) {
+        barrier_vm<63>();  // tile buffers 0 are read no more
+        issue_kv(K + nhead, V + nhead);
+      }
+      ++seq;
+      vb = nvb;
+      k = nk;
+      cbh = nbh;
+      cqb = nqb;
+      have = next;
     }
   }
   if constexpr (!BIAS) {
+    pf_q = pf_kv = false;
     barrier_vm<63>();  // every flag is written, every tile read
     int s = 0;
     for (uint32_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
-      const uint32_t unit = set_unit(vb);
-      const uint32_t partner = CAUSAL ? n_qblk - 1 - unit : unit;
-      for (int k = 0; k < (CAUSAL && partner != unit ? 2 : 1); ++k, ++s) {
+      for (int k = 0; k < (CAUSAL ? 2 : 1); ++k) {
+        uint32_t b, qb;
+        if (!locate(vb, k, b, qb)) continue;
         if (__builtin_amdgcn_readfirstlane(redo[s]) != 0) {
-          const uint32_t qb = k == 0 ? partner : unit;
-          issue(qb);
+          set_head(b);
+          issue_q(Q + head, qb);
+          issue_kv(Kh, Vh);
           body(qb, SAFEC{});
           barrier_vm<63>();
         }
+        ++s;
       }
     }
   }
