@@ -587,8 +587,10 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   // O through 2 KiB of LDS per wave in K tile buffer 1 (free during the last
   // tile, whatever its parity), 32 head dims at a time: the lane's four runs
   // of 4 dims go in as 8-byte writes ([32 rows][64 bytes], 16-byte chunks
-  // XOR-swizzled by row / 4), and leave as 16-byte reads of 16 rows x 64
-  // bytes per instruction, stored as 64 contiguous bytes per row.
+  // XOR-swizzled by row / 4, and the two 8-byte halves of a chunk swapped in
+  // rows 16..31, so that 32 lanes' writes meet 64 different banks), and
+  // leave as 16-byte reads of 16 rows x 64 bytes per instruction, stored as
+  // 64 contiguous bytes per row.
   uint16_t* const low = lk1 + wave * 1024;
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) {
@@ -597,12 +599,14 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
       bf16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[cb][4 * q4 + e] * inv);
-      *reinterpret_cast<bf16x4*>(low + r_e * 32 + ((q4 ^ ((r_e >> 2) & 3)) << 3) + 4 * g_e) = v;
+      *reinterpret_cast<bf16x4*>(low + r_e * 32 + ((q4 ^ ((r_e >> 2) & 3)) << 3) +
+                                 4 * (g_e ^ (r_e >> 4))) = v;
     }
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int row = 16 * x + (ln_e >> 2), c = ln_e & 3;
-      const bf16x8 w = lds_read_b128(low + row * 32 + ((c ^ ((row >> 2) & 3)) << 3));
+      bf16x8 w = lds_read_b128(low + row * 32 + ((c ^ ((row >> 2) & 3)) << 3));
+      if (x == 1) w = __builtin_shufflevector(w, w, 4, 5, 6, 7, 0, 1, 2, 3);  // (halves swapped in rows 16..31)
       if (q0 + row < N) *reinterpret_cast<bf16x8*>(O + head + (size_t)(q0 + row) * D + 32 * cb + 8 * c) = w;
     }
   }
