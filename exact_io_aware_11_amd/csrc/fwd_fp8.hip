@@ -100,6 +100,12 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t lk1[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lv0[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lv1[TILE];
+  // Each wave's rows: its 32 Q rows come in (as whole rows, 16-byte direct
+  // loads; 16-byte chunks XOR-swizzled by row / 2 at D = 128, row / 4 at
+  // D = 64), and its 32 rows of O (bfloat16) go out through the same space,
+  // so that both cross HBM as 16-byte accesses of consecutive addresses
+  // instead of 16 (or 8) bytes from each of 32 rows per instruction.
+  __shared__ __attribute__((aligned(1024))) uint8_t lrow[4 * 32 * 2 * D];
   auto ktile = [&](auto bufc) __attribute__((always_inline)) -> uint8_t* {
     if constexpr (decltype(bufc)::value == 0) return lk0;
     else return lk1;
@@ -136,19 +142,23 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   const int qrow = q0 + r32;
 
   // Q as the B operand: lane holds Q[qrow][64t + 16g .. +15] and
-  // Q[qrow][64t + 32 + 16g .. +15].
-  i32x8 qf[NT];
+  // Q[qrow][64t + 32 + 16g .. +15] -- from the wave's LDS rows, read once
+  // they have landed (with the first tiles, below).
+  uint8_t* const lrw = lrow + wave * 32 * 2 * D;
+  auto qrow_byte = [](int row, int chunk) __attribute__((always_inline)) {
+    return row * D + 16 * (chunk ^ (D == 128 ? (row >> 1) & 7 : (row >> 2) & 3));
+  };
+  {
+    const auto qres = make_tile_rsrc<D>(Q + head + (size_t)q0 * D, N - q0);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (qrow < N) {
-      const uint8_t* p = Q + head + (size_t)qrow * D + 64 * t + 16 * g;
-      const i32x4 a = *reinterpret_cast<const i32x4*>(p);
-      const i32x4 b = *reinterpret_cast<const i32x4*>(p + 32);
-      qf[t] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-    } else {
-      qf[t] = i32x8{};
+    for (int x = 0; x < D / 32; ++x) {
+      const int byte = x * 1024 + 16 * lane, row = byte / D, chunk = (byte % D) >> 4;
+      // (the lane fetches the logical chunk that the swizzle puts at its byte)
+      const int lchunk = chunk ^ (D == 128 ? (row >> 1) & 7 : (row >> 2) & 3);
+      load_lds16(qres, lrw + x * 1024, (uint32_t)(row * D + 16 * lchunk));
     }
   }
+  i32x8 qf[NT];
   // MX: this row's four (D = 128) or two block scales in one word, shifted so
   // that byte 2t is the scale of this lane's k block of product t.
   uint32_t qsc = 0x7f7f7f7fu;
@@ -315,6 +325,12 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
   stage_kscale(lks0, 0);
   stage_vscale(lvs0, 0);
   barrier_vm<0>();
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const i32x4 a = lds_read_i32x4(lrw + qrow_byte(r32, 4 * t + g));
+    const i32x4 b = lds_read_i32x4(lrw + qrow_byte(r32, 4 * t + 2 + g));
+    qf[t] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
   stage(Kh, lk1, BN);
   stage_kscale(lks1, BN);
   scores(lk0, lks0, sa0, sa1);
@@ -471,19 +487,29 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
 
   const float l_tot = halves_sum(l_run);
   const float f = out_scale / l_tot;
-  if (qrow < N) {
-    uint16_t* Orow = O + head + (size_t)qrow * D;
+  // O through the wave's LDS rows (bfloat16 rows of 2 D bytes, the bf16
+  // tiles' swizzle): four runs of 4 head dims per 32 in as 8-byte writes,
+  // whole rows out as 16-byte reads, stored 1 KiB of consecutive rows per
+  // instruction.  (Row and half formed from a fresh lane id.)
+  uint16_t* const low = reinterpret_cast<uint16_t*>(lrw);
+  const int ln_e = lane_id_here();
+  const int r_e = ln_e & 31, g_e = ln_e >> 5;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 v;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[cb][4 * q4 + e] * f);
-        *reinterpret_cast<bf16x4*>(Orow + 32 * cb + 8 * q4 + 4 * g) = v;
-      }
-    if (g == 0) LSE[(size_t)bh * N + qrow] = m_run * lse_scale + __logf(l_tot) - 8.f * kLn2;
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[cb][4 * q4 + e] * f);
+      *reinterpret_cast<bf16x4*>(low + tile_off<D>(r_e, 4 * cb + q4) + 4 * g_e) = v;
+    }
+#pragma unroll
+  for (int x = 0; x < D / 16; ++x) {
+    const int byte = x * 1024 + 16 * ln_e, row = byte / (2 * D), chunk = (byte % (2 * D)) >> 4;
+    const bf16x8 w = lds_read_b128(low + tile_off<D>(row, chunk));
+    if (q0 + row < N) *reinterpret_cast<bf16x8*>(O + head + (size_t)(q0 + row) * D + 8 * chunk) = w;
   }
+  if (g_e == 0 && q0 + r_e < N) LSE[(size_t)bh * N + q0 + r_e] = m_run * lse_scale + __logf(l_tot) - 8.f * kLn2;
 }
 
 template <int D, bool CAUSAL, bool MX>
