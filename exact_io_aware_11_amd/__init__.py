@@ -17,11 +17,13 @@ C names:
 * :func:`fa_std_fwd`, :func:`fa_std_workspace_size` -- standard attention with
   S and P written to device memory: the baseline of the IO comparison
 * :func:`fa_bwd_workspace_size`, :func:`fa_status_string`
-* :func:`fa_measure_mfma_rate` -- a measurement aid: the matrix-core rate on
-  realistic operand bits, against which the kernels' rates are also read
+* :func:`fa_measure_mfma_rate` (module :mod:`.probe`, library libfa_probe.so,
+  include/fa_probe.h) -- a measurement aid outside the attention library: the
+  matrix-core rate on realistic operand bits, against which the kernels'
+  rates are also read
 
-There is no fallback: if the shared library is missing or fails to load, the
-import of :mod:`exact_io_aware_11_amd._lib` raises.
+There is no fallback: if a shared library is missing or fails to load, the
+import of :mod:`exact_io_aware_11_amd._lib` (or :mod:`.probe`) raises.
 """
 from __future__ import annotations
 
@@ -29,8 +31,9 @@ from ._lib import (FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, 
                    FA_FP8_E4M3, FA_NOALLOC_MAX_ROWS, FA_OK, FAError, lib)
 from .api import (dtype_code, fa_bwd, fa_bwd_bias, fa_bwd_delta, fa_bwd_dkdv, fa_bwd_dq,
                   fa_bwd_noalloc,
-                  fa_bwd_workspace_size, fa_fwd, fa_fwd_bias, fa_fwd_mxfp8, fa_measure_mfma_rate,
+                  fa_bwd_workspace_size, fa_fwd, fa_fwd_bias, fa_fwd_mxfp8,
                   fa_status_string, fa_std_fwd, fa_std_workspace_size, flops_bwd, flops_fwd)
+from .probe import fa_measure_mfma_rate
 
 __all__ = [
     "FA_FP32", "FA_BF16", "FA_FP8_E4M3", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",

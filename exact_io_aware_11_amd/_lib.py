@@ -27,7 +27,6 @@ SIGNATURES = {
                          _sz, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_bwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i,
                             _i, _vp]),
-    "fa_measure_mfma_rate": (_i, [_vp, _i, _i, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
 }
 for _stage in ("fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq"):
@@ -42,7 +41,7 @@ class FAError(RuntimeError):
         super().__init__(f"{what}: status {status}")
 
 
-def _load() -> ctypes.CDLL:
+def _check_loaded_torch() -> None:
     # torch must be loaded first: its HIP runtime carries the soname
     # libamdhip64.so.7 that libfa.so asks for, so both share ONE runtime (and
     # torch's streams and allocations are valid for our launches).  Loading
@@ -50,6 +49,9 @@ def _load() -> ctypes.CDLL:
     # for the unversioned name, would then load its own copy next to it.
     import torch  # noqa: F401
 
+
+def _load() -> ctypes.CDLL:
+    _check_loaded_torch()
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python exact_io_aware_11_amd/build.py` "

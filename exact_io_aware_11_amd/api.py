@@ -278,22 +278,6 @@ def fa_bwd_dq(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, strea
     _bwd_call("fa_bwd_dq", q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, stream)
 
 
-def fa_measure_mfma_rate(out, blocks: int, iters: int, fp8: bool = False, stream=None):
-    """Enqueue the matrix-core rate probe (a measurement aid, see include/fa.h);
-    out is a float32 device tensor of at least blocks * 512 elements.  Returns
-    the FLOPs the launch performs."""
-    import torch
-
-    _check_device("out", out)
-    if out.dtype != torch.float32 or out.numel() < blocks * 512:
-        raise ValueError("out must be float32 with blocks * 512 elements")
-    st = lib.fa_measure_mfma_rate(out.data_ptr(), int(blocks), int(iters),
-                                  FA_FP8_E4M3 if fp8 else FA_BF16, _stream_handle(stream))
-    if st != FA_OK:
-        raise FAError(st, "fa_measure_mfma_rate: " + fa_status_string(st))
-    return float(blocks) * 8 * iters * 8 * (131072 if fp8 else 32768)
-
-
 def fa_status_string(status: int) -> str:
     return lib.fa_status_string(int(status)).decode()
 

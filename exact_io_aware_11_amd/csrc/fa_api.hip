@@ -385,14 +385,6 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void
   return launch_bwd(a, dtype, kStageDelta | kStageDkDv | kStageDq);
 }
 
-fa_status fa_measure_mfma_rate(float* out, int blocks, int iters, int dtype, void* stream) {
-  if (dtype != FA_BF16 && dtype != FA_FP8_E4M3) return dtype == FA_FP32 ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
-  if (!out || !aligned(out, 4) || blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 20))
-    return FA_ERR_INVALID_ARG;
-  return fa::launch_mfma_peak(out, blocks, iters, dtype == FA_FP8_E4M3, (hipStream_t)stream) == hipSuccess
-             ? FA_OK : FA_ERR_HIP;
-}
-
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

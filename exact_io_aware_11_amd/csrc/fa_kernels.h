@@ -96,6 +96,5 @@ hipError_t launch_dq_f32(const BwdArgs& a);
 hipError_t launch_dkdv_bf16(const BwdArgs& a);
 hipError_t launch_dq_bf16(const BwdArgs& a);  // also writes delta (from O and dO)
 hipError_t launch_std_bf16(const StdArgs& a);
-hipError_t launch_mfma_peak(float* out, int blocks, int iters, bool fp8, hipStream_t stream);
 
 }  // namespace fa

@@ -4,9 +4,12 @@
 // data whose bits toggle like real inputs -- the chip lowers its clock to
 // stay within its power budget, so this rate sits below the published peak.
 // The caller times the launch; the kernel writes one float per thread so that
-// nothing is optimised away.  Not part of the attention path.
+// nothing is optimised away.  Not part of the attention path: it is built
+// into its own library (libfa_probe.so, include/fa_probe.h).
+#include <stdint.h>
+
 #include "fa_device.h"
-#include "fa_kernels.h"
+#include "fa_probe.h"
 
 namespace fa {
 
@@ -75,10 +78,18 @@ __global__ __launch_bounds__(512, 1) void mfma_peak_kernel(float* __restrict__ o
   out[blockIdx.x * 512u + threadIdx.x] = s;
 }
 
-hipError_t launch_mfma_peak(float* out, int blocks, int iters, bool fp8, hipStream_t stream) {
-  if (fp8) hipLaunchKernelGGL(mfma_peak_kernel<true>, dim3(blocks), dim3(512), 0, stream, out, iters);
-  else hipLaunchKernelGGL(mfma_peak_kernel<false>, dim3(blocks), dim3(512), 0, stream, out, iters);
-  return hipGetLastError();
-}
-
 }  // namespace fa
+
+extern "C" int fa_measure_mfma_rate(float* out, int blocks, int iters, int dtype, void* stream) {
+  if (dtype != FA_PROBE_BF16 && dtype != FA_PROBE_FP8_E4M3)
+    return dtype == FA_PROBE_FP32 ? FA_PROBE_ERR_UNSUPPORTED : FA_PROBE_ERR_INVALID_ARG;
+  if (!out || ((uintptr_t)out & 3u) != 0 || blocks < 1 || blocks > 65536 || iters < 1 ||
+      iters > (1 << 20))
+    return FA_PROBE_ERR_INVALID_ARG;
+  const hipStream_t st = (hipStream_t)stream;
+  if (dtype == FA_PROBE_FP8_E4M3)
+    hipLaunchKernelGGL(fa::mfma_peak_kernel<true>, dim3(blocks), dim3(512), 0, st, out, iters);
+  else
+    hipLaunchKernelGGL(fa::mfma_peak_kernel<false>, dim3(blocks), dim3(512), 0, st, out, iters);
+  return hipGetLastError() == hipSuccess ? FA_PROBE_OK : FA_PROBE_ERR_HIP;
+}

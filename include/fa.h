@@ -233,20 +233,6 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void
                          const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                          int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
-/* Measurement aid, not part of attention: enqueues a pure stream of 32x32
- * matrix-core products (bf16 32x32x16 or fp8 32x32x64, FLOPs per product
- * 32768 or 131072) on fixed pseudo-random per-lane operands, `blocks`
- * workgroups of 512 threads (two waves per SIMD; use a multiple of the CU
- * count), each thread running iters * 8 products; every thread writes one
- * float to out[block * 512 + thread] (the caller provides blocks * 512 floats
- * of device memory).  Timing the launch gives the rate the matrix cores
- * sustain on realistic operand bits at the clock the chip settles to -- the
- * measured peak that attention kernels are compared with besides the
- * published one.  Total FLOPs = blocks * 8 waves * iters * 8 * (FLOPs per
- * product).  dtype FA_BF16 or FA_FP8_E4M3 (FA_FP32: FA_ERR_UNSUPPORTED);
- * blocks 1..65536, iters 1..2^20. */
-fa_status fa_measure_mfma_rate(float* out, int blocks, int iters, int dtype, void* stream);
-
 /* Static, NUL-terminated description of a status code (never NULL).  The
  * pages define no error convention; the codes are this library's own. */
 const char* fa_status_string(int status);

@@ -10,6 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "fa_probe.h")
 
 fa = pytest.importorskip("exact_io_aware_11_amd")
 lib = fa.lib
@@ -18,8 +19,8 @@ OK, INVALID, UNSUPPORTED = fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTE
 P = 0x10000  # a 16-byte aligned fake address; never dereferenced in these tests
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
 
@@ -27,9 +28,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_bias", "fa_bwd_delta", "fa_bwd_dkdv",
                                     "fa_bwd_dq", "fa_bwd_noalloc", "fa_bwd_workspace_size",
-                                    "fa_fwd",
-                                    "fa_fwd_bias", "fa_fwd_mxfp8", "fa_measure_mfma_rate",
+                                    "fa_fwd", "fa_fwd_bias", "fa_fwd_mxfp8",
                                     "fa_status_string", "fa_std_fwd", "fa_std_workspace_size"]
+    assert declared_functions(PROBE_HEADER) == ["fa_measure_mfma_rate"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -37,6 +38,22 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(raw, name), name
     assert set(fa._lib.SIGNATURES) == set(declared_functions())
+    # the rate probe lives in its own library, not in the attention one
+    assert not hasattr(raw, "fa_measure_mfma_rate")
+    probe = ctypes.CDLL(fa.probe.PROBE_LIB_PATH)
+    for name in declared_functions(PROBE_HEADER):
+        assert hasattr(probe, name), name
+    assert set(fa.probe.SIGNATURES) == set(declared_functions(PROBE_HEADER))
+
+
+def test_probe_status_codes_match_the_attention_ones():
+    """fa_probe.h repeats fa.h's element-type and status values."""
+    def enum_values(header):
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        return {k: int(v) for k, v in re.findall(r"\b(FA_[A-Z0-9_]+)\s*=\s*(\d+)", text)}
+    main, probe = enum_values(HEADER), enum_values(PROBE_HEADER)
+    for name in ("FP32", "BF16", "FP8_E4M3", "OK", "ERR_INVALID_ARG", "ERR_UNSUPPORTED", "ERR_HIP"):
+        assert probe["FA_PROBE_" + name] == main["FA_" + name], name
 
 
 def fwd(**kw):
@@ -192,7 +209,7 @@ def test_bwd_noalloc_empty_is_a_noop():
     ((P, 65537, 10, 1), INVALID), ((P, 256, 0, 2), INVALID), ((P, 256, 1 << 21, 1), INVALID),
     ((P, 256, 10, 0), UNSUPPORTED), ((P, 256, 10, 7), INVALID)])
 def test_rate_probe_rejects_before_launch(args, status):
-    assert lib.fa_measure_mfma_rate(*args, None) == status
+    assert fa.probe.probe_lib.fa_measure_mfma_rate(*args, None) == status
 
 
 def std(**kw):
