@@ -291,6 +291,22 @@ def test_bf16_block_orders(B, H, N, d, causal):
     full_check_bwd(inp, 1 / math.sqrt(d), causal, f"bf16 order {B}x{H}x{N}x{d}")
 
 
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 128, 1064, 128, False),  # 640 units of 256 rows: 2-3 per workgroup, 17 key tiles (odd)
+    (1, 128, 1064, 128, True),   # 384 pairs (one of a single block per head), last block 17 tiles
+    (1, 256, 1064, 64, False),   # 2304 units of 128 rows over 3 workgroups per CU
+    (1, 256, 1064, 64, True),    # 1280 pairs, 9 row blocks per head (odd: a one-block pair)
+])
+def test_bf16_forward_walks(B, H, N, d, causal):
+    """The bf16 forward's workgroups (one per CU slot) walk several units back
+    to back: each block's first loads are issued at the previous block's last
+    barrier, or after one more barrier when that block ended on an even tile
+    index (odd tile count) -- both kinds, pairs of one block, ragged N, every
+    output against the oracle."""
+    inp = fa_inputs.make_inputs((B, H, N, d), "bf16", seed=H + N + d, with_dout=False)
+    full_check_fwd(inp, 1 / math.sqrt(d), causal, f"bf16 walk {B}x{H}x{N}x{d}")
+
+
 @pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, False), ("bf16", 128, True),
                                              ("bf16", 64, True), ("fp8", 128, False)])
 def test_longest_sequence_forward(dtype, d, causal):
