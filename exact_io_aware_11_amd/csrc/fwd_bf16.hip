@@ -318,24 +318,45 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     }
   };
 
-  // Masked scores: keys past N, and under the causal mask keys after the query.
+  // Masked scores: keys past N, and under the causal mask keys after the
+  // query.  Element i of key half h of a tile at key0 is key key0 + 32 h +
+  // 8 (i / 4) + 4 g + i % 4; it is visible iff it is at most lim = N - 1
+  // (causal: min(N - 1, qrow)).  With t = lim - key0 - 4 g (one value per lane
+  // and tile) that is 32 h + 8 (i / 4) + i % 4 <= t: one compare with a
+  // constant per element.  (The lane's row is formed from the lane id here,
+  // not held through the scan.)
+  auto mask_thr = [&](int key0) __attribute__((always_inline)) -> int {
+    const int ln = lane_id_here();
+    const int lim = CAUSAL ? min(N - 1, q0 + (ln & 31)) : N - 1;
+    return lim - key0 - 4 * (ln >> 5);
+  };
+  auto mask_elem = [&](f32x16 (&s)[NH], int i, int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+      if (32 * h + 8 * (i >> 2) + (i & 3) > t) s[h][i] = -INFINITY;
+  };
   auto apply_mask = [&](f32x16 (&s)[NH], int key0) __attribute__((always_inline)) {
+    const int t = mask_thr(key0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = key0 + 8 * (i >> 2) + 4 * g + (i & 3);
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-        if (key + 32 * h >= N || (CAUSAL && key + 32 * h > qrow)) s[h][i] = -INFINITY;
-    }
+    for (int i = 0; i < 16; ++i) mask_elem(s, i, t);
   };
 
+  // Causal without a bias: this wave's tiles end at n_use, the last one with
+  // a key at or before its last query; the workgroup's diagonal tiles past
+  // it would give all-zero P and all-masked scores.  The wave stops its
+  // products there, and for the rest of the workgroup's tiles only stages its
+  // share and meets the barriers (its SIMD partner has the matrix core to
+  // itself meanwhile).
+  const int n_use = CAUSAL && !BIAS ? min(n_tiles, (q0 + 31) / BN + 1) : n_tiles;
   // Software pipeline: K runs one tile ahead of V.  At step j the LDS holds
   // K_{j+1} and V_j, and the registers hold S_j = K_j Q^T, masked, with its
-  // reference max settled.  Tiles [0, j_full) need no mask for any row of the
-  // workgroup; the causal diagonal tiles and a ragged tail are masked while
-  // their scores are formed.  The two score buffers swap roles with the step
-  // parity, so nothing is copied.
-  const int j_full = min(CAUSAL ? (int)qblk * (BM / BN) : n_tiles, N / BN);
+  // reference max settled.  Tiles [0, j_full) need no mask for this wave's
+  // rows; the rest (the causal diagonal, a ragged tail) are masked while
+  // their scores are formed.  Causal without a bias, only the wave's last
+  // tile: the wave's first row q0 is a multiple of 32, so every key of an
+  // earlier 64-key tile lies before q0 and inside N.  The two score buffers
+  // swap roles with the step parity, so nothing is copied.
+  const int j_full = CAUSAL && !BIAS ? n_use - 1 : min(CAUSAL ? (int)qblk * (BM / BN) : n_tiles, N / BN);
   f32x16 sa[NH], sb[NH];  // scores of even (a) and odd (b) tiles, by key half
   auto sc_of = [&](auto parity) __attribute__((always_inline)) -> f32x16 (&)[NH] {
     if constexpr (decltype(parity)::value == 0) return sa;
@@ -448,12 +469,7 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
       sv[i] = x;
       if (ph == 2 && (e & 7) == 7) pk[e >> 3] = to_bf16x8(sv, i - 7);
     };
-    auto mask_next = [&](int i) __attribute__((always_inline)) {  // element i of each half of S_{j+1}
-      const int key = key1 + 8 * (i >> 2) + 4 * g + (i & 3);
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-        if (key + 32 * h >= N || (CAUSAL && key + 32 * h > qrow)) sn[h][i] = -INFINITY;
-    };
+    int mthr = 0;  // mask threshold of S_{j+1}, formed where its masking starts
     // Elements start phase (a) over products 0 .. EXP_OPS-1; phase (c) of the
     // last element of key chunk kc lands two products later, before product
     // NS + kc (D/32), the chunk's first PV product.
@@ -469,9 +485,11 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
       }
       if (k >= NOPS - MAX_OPS) {  // row max of S_{j+1} over the last MAX_OPS products
         const int r = k - (NOPS - MAX_OPS);
+        if constexpr (MASK_NEXT)
+          if (r == 0) mthr = mask_thr(key1);
 #pragma unroll
         for (int i = r * 16 / MAX_OPS; i < (r + 1) * 16 / MAX_OPS; ++i) {
-          if constexpr (MASK_NEXT) mask_next(i);
+          if constexpr (MASK_NEXT) mask_elem(sn, i, mthr);
           if constexpr (!FAST) {
             mxp[i & 1] = fmaxf(mxp[i & 1], NH == 2 ? fmaxf(sn[0][i], sn[NH - 1][i]) : sn[0][i]);
             pin(mxp[i & 1]);
@@ -528,26 +546,27 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     exps(sc_of(parity), p);
     pv(vtile(parity), p);
   };
-  // Steps whose next tile is full, then the rest (masking the next tile's
-  // scores is correct for any tile, just slower), then the last tile.
+  // Step j forms S_{j+1}, masked iff j + 1 >= j_full; steps run in pairs (the
+  // parity picks the buffers), then the last tile.
   using NOMASK = std::false_type;
   using MASK = std::true_type;
-  // Causal without a bias: this wave's tiles end at n_use, the last one with
-  // a key at or before its last query; the workgroup's diagonal tiles past
-  // it would give all-zero P and all-masked scores.  The wave stops its
-  // products there, and for the rest of the workgroup's tiles only stages its
-  // share and meets the barriers (its SIMD partner has the matrix core to
-  // itself meanwhile).  j_full < n_use always: the block's first row sees
-  // every key before the block.
-  const int n_use = CAUSAL && !BIAS ? min(n_tiles, (q0 + 31) / BN + 1) : n_tiles;
   int j = 0;
   for (; j + 2 < j_full; j += 2) {
     step(B0{}, NOMASK{}, j);
     step(B1{}, NOMASK{}, j + 1);
   }
-  for (; j + 2 < n_use; j += 2) {
-    step(B0{}, MASK{}, j);
-    step(B1{}, MASK{}, j + 1);
+  if constexpr (CAUSAL && !BIAS) {
+    // j_full = n_use - 1: only the step forming the wave's last tile masks
+    if (j + 2 == j_full) {
+      step(B0{}, NOMASK{}, j);
+      step(B1{}, MASK{}, j + 1);
+      j += 2;
+    }
+  } else {
+    for (; j + 2 < n_use; j += 2) {
+      step(B0{}, MASK{}, j);
+      step(B1{}, MASK{}, j + 1);
+    }
   }
   if (j + 1 < n_use) {  // two tiles left
     step(B0{}, MASK{}, j);
