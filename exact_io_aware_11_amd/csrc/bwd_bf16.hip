@@ -59,7 +59,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   uint32_t bh, kblk;
-  map_block(blockIdx.x, n_kblk, total, CAUSAL ? kOrderHeavyFirst : kOrderPlain, bh, kblk);
+  if (BIAS && bias.grouped) map_block_grouped(blockIdx.x, n_kblk, total, bias.grouped, false, bh, kblk);
+  else map_block(blockIdx.x, n_kblk, total, CAUSAL ? kOrderHeavyFirst : kOrderPlain, bh, kblk);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* Qh = Q + head;
   const uint16_t* dOh = dO + head;
@@ -397,7 +398,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   uint32_t bh, qblk;
-  map_block(blockIdx.x, n_qblk, total, CAUSAL ? kOrderHeavyLast : kOrderPlain, bh, qblk);
+  if (BIAS && bias.grouped) map_block_grouped(blockIdx.x, n_qblk, total, bias.grouped, CAUSAL, bh, qblk);
+  else map_block(blockIdx.x, n_qblk, total, CAUSAL ? kOrderHeavyLast : kOrderPlain, bh, qblk);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
@@ -682,10 +684,14 @@ template <int D, bool CAUSAL, bool BIAS>
 static hipError_t dkdv_bf16_t(const BwdArgs& a) {
   const uint32_t n_kblk = (uint32_t)((a.N + 127) / 128);
   const uint32_t total = (uint32_t)(a.BH * n_kblk);
+  Bias bias = a.bias;
+  // (causal: the heavy-first order already walks several heads block-major, and
+  // groups would leave the heavy key blocks of a head group to one XCD)
+  bias.grouped = CAUSAL ? 0 : group_blocks(bias, a.BH, n_kblk, 4);  // one workgroup per CU: 32 per XCD
   hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, BIAS>), dim3(total), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     a.N, n_kblk, total, a.scale, a.scale * kLog2e, a.bias);
+                     a.N, n_kblk, total, a.scale, a.scale * kLog2e, bias);
   return hipGetLastError();
 }
 
@@ -693,10 +699,12 @@ template <int D, bool CAUSAL, bool BIAS>
 static hipError_t dq_bf16_t(const BwdArgs& a) {
   const uint32_t n_qblk = (uint32_t)((a.N + 127) / 128);
   const uint32_t total = (uint32_t)(a.BH * n_qblk);
+  Bias bias = a.bias;
+  bias.grouped = CAUSAL ? 0 : group_blocks(bias, a.BH, n_qblk, 8);  // two workgroups per CU: 64 per XCD
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, BIAS>), dim3(total), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, (const uint16_t*)a.o, a.lse, a.delta,
-                     (uint16_t*)a.dq, a.N, n_qblk, total, a.scale, a.scale * kLog2e, a.bias);
+                     (uint16_t*)a.dq, a.N, n_qblk, total, a.scale, a.scale * kLog2e, bias);
   return hipGetLastError();
 }
 

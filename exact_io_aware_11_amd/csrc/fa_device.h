@@ -209,6 +209,36 @@ __device__ __forceinline__ void map_block(uint32_t w, uint32_t n_blk, uint32_t t
   if (order == kOrderHeavyLast) blk = n_blk - 1u - blk;
 }
 
+// Mapping for a bias shared by the heads of a batch entry.  With map_block's
+// plain order the workgroups that run together on one XCD take every block of
+// one or two heads: they share those heads' tiles in L2, but each head reads
+// the whole bias again.  Here the XCD's range of total/8 logical blocks is
+// cut into groups of kGroupHeads heads x U blocks, heads minor, with U chosen
+// so that a group is about what one XCD runs at once: each bias tile is then
+// read by kGroupHeads workgroups and each Q/K/V tile by U, at about the same
+// time.  Blocks ascend across groups (heavy first for causal key blocks);
+// heavy_last reverses them (causal row blocks).  Requires total % 8 == 0,
+// heads % kGroupHeads == 0 and n_blk % U == 0 (then it is a permutation).
+constexpr uint32_t kGroupHeads = 8;
+__device__ __forceinline__ void map_block_grouped(uint32_t w, uint32_t n_blk, uint32_t total,
+                                                  uint32_t U, bool heavy_last, uint32_t& bh,
+                                                  uint32_t& blk) {
+  const uint32_t logical = (w & 7u) * (total >> 3) + (w >> 3);
+  const uint32_t G = kGroupHeads * U;
+  const uint32_t grp = logical / G, in = logical - grp * G;
+  const uint32_t per_head_group = n_blk / U;  // block groups per head group
+  const uint32_t hg = grp / per_head_group, bg = grp - hg * per_head_group;
+  bh = hg * kGroupHeads + in % kGroupHeads;
+  blk = bg * U + in / kGroupHeads;
+  if (heavy_last) blk = n_blk - 1u - blk;
+}
+
+// Blocks per group for a launch over bh_count heads x n_blk blocks, or 0 when
+// the grouped order does not apply (host side).
+inline int group_blocks(const Bias& b, long bh_count, uint32_t n_blk, uint32_t want) {
+  return b.p && b.sh == 0 && bh_count % (long)kGroupHeads == 0 && n_blk % want == 0 ? (int)want : 0;
+}
+
 // 16-byte-chunk XOR swizzle of a [rows][D] bf16 tile in LDS (D = 64 or 128).
 // It serves the two read patterns the kernels use, both free of bank
 // conflicts (64 banks x 4 bytes):

@@ -17,6 +17,11 @@ struct Bias {
   long long sb = 0, sh = 0, sq = 0;
   int H = 1;  // heads per batch entry: splits the combined index bh into (b, h)
   uint32_t head_bytes = 0;
+  // Set by a launcher when every head of a batch entry reads the same bias
+  // (sh = 0) and the grid allows it: workgroups running together on one XCD
+  // then take kGroupHeads heads x `grouped` blocks (map_block_grouped);
+  // 0: map_block's order.
+  int grouped = 0;
 };
 
 // Forward schedules of the bf16 d = 128 kernels without a bias (the

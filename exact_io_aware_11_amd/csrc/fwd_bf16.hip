@@ -654,7 +654,8 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   auto locate = [&](uint32_t vb, int k, uint32_t& bh_o, uint32_t& qb_o) __attribute__((always_inline)) -> bool {
     if (vb >= total) return false;
     uint32_t unit;
-    map_block(vb, n_units, total, kOrderPlain, bh_o, unit);
+    if (BIAS && bias.grouped) map_block_grouped(vb, n_units, total, bias.grouped, false, bh_o, unit);
+    else map_block(vb, n_units, total, kOrderPlain, bh_o, unit);
     const uint32_t partner = CAUSAL ? n_qblk - 1 - unit : unit;
     qb_o = k == 0 ? partner : unit;
     return k == 0 || partner != unit;
@@ -765,10 +766,12 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   // bound by its bias traffic, measured 10 % slower with the static walk than
   // with the hardware handing out units as CUs free up.)
   const uint32_t grid = BIAS ? total : (uint32_t)std::min<uint64_t>(total, std::max(slots, least));
+  Bias bias = a.bias;
+  bias.grouped = group_blocks(bias, a.BH, n_units, 8);  // two workgroups per CU: 64 per XCD
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WAVES, BIAS>), dim3(grid), dim3(64 * WAVES), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, n_qblk, total, a.scale, a.scale * kLog2e,
-                     kRescaleLog2 / (a.scale * kLog2e), a.bias);
+                     kRescaleLog2 / (a.scale * kLog2e), bias);
   return hipGetLastError();
 }
 

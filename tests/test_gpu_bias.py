@@ -145,6 +145,25 @@ def test_bf16_broadcast_biases(N, kind, causal):
     check_case(inp, b, 1 / math.sqrt(d), causal, f"bf16 {kind} bias 2x3x{N}x{d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["shared", "keypad"])
+def test_bf16_bias_grouped_order(kind, causal, d):
+    """Biases that every head of a batch entry shares (head stride 0) on grids
+    where the bf16 forward groups its workgroups by 8 heads x 8 row blocks
+    (8 heads per batch entry, 8 blocks or causal pairs of blocks per head):
+    every output against the full oracle, forward and backward."""
+    N = 2048 if causal else 1024
+    B = 2 if kind == "keypad" else 1
+    inp = fa_inputs.make_inputs((B, 8, N, d), "bf16", seed=31 * d + int(causal))
+    if kind == "shared":      # one [N, N] bias (10 % -inf) for every head
+        b = fa_inputs.draw_bias((1, 1), N, seed=d, kind="dense")
+    else:                     # [B, 1, 1, N]: per-batch key lengths
+        b = fa_inputs.draw_bias((B, 1), N, seed=d, kind="keypad")
+    check_case(inp, b, 1 / math.sqrt(d), causal,
+               f"bf16 {kind} bias {B}x8x{N}x{d} causal={causal} (grouped order)")
+
+
 @pytest.mark.parametrize("N", [1, 65, 257])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
@@ -221,6 +240,18 @@ def test_full_bf16_causal_bias_fwd_b2h32n8192d128():
         dead = check_lse(f"{tag} LSE rows", lse64[b, h, rows], lse_ref, "bf16")
         assert np.all(o64[b, h, rows][dead] == 0.0)
         check(f"{tag} O rows", o64[b, h, rows], o_ref, "bf16")
+    # every (b, h) at a few rows: first and last of the first block, one in
+    # the middle that moves with the head, the last (the grouped block order)
+    for b in range(B):
+        for h in range(H):
+            few = np.array(sorted({0, 127, 128 + 61 * (b * H + h) % (N - 256), N - 1}))
+            qs, ks, vs = (exact_values(x[b, h], "bf16") for x in (inp.q, inp.k, inp.v))
+            o_ref, lse_ref = oracle.attn_fwd_rows(qs, ks, vs, few, scale, True,
+                                                  bias_rows=b_np[0, 0, few, :N].astype(np.float64))
+            tag = f"dense bias 2x32x8192x128 head ({b},{h}) rows {few.tolist()}"
+            dead = check_lse(f"{tag} LSE", lse64[b, h, few], lse_ref, "bf16")
+            assert np.all(o64[b, h, few][dead] == 0.0)
+            check(f"{tag} O", o64[b, h, few], o_ref, "bf16")
 
 
 @pytest.mark.parametrize("d", [64, 128])
