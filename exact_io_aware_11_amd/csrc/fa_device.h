@@ -113,6 +113,13 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, const void*
                                            voff, 0, 0, 0);
 }
 
+// The same with a wave-uniform byte offset soff added (scalar operand).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, const void* dst, uint32_t voff,
+                                           uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, soff, 0, 0);
+}
+
 // Direct load of 4 bytes per lane (256 bytes per wave) to LDS at dst + 4 * lane.
 __device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, const void* dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4,

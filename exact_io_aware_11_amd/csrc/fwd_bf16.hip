@@ -90,13 +90,17 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  // per block of this workgroup, in order: set when the FAST path must be
-  // redone (zeroed here, before the first barrier)
-  __shared__ int redo[kFwdMaxSeq];
+  // With a bias, the bias tiles: each wave stages the rows of its own 32
+  // queries, BN float32 keys each (below).  Without, per block of this
+  // workgroup, in order: set when the FAST path must be redone (zeroed here,
+  // before the first barrier).  (Two bias workgroups per CU use all 160 KiB.)
+  __shared__ __attribute__((aligned(1024))) int lside[BIAS ? BM * BN : kFwdMaxSeq];
+  int* const redo = lside;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  for (int i = tid; i < kFwdMaxSeq; i += 64 * WAVES) redo[i] = 0;
+  if constexpr (!BIAS)
+    for (int i = tid; i < kFwdMaxSeq; i += 64 * WAVES) redo[i] = 0;
   const int g = lane >> 5, r32 = lane & 31;
   // Causal: a workgroup takes row blocks u and n_qblk - 1 - u, which together
   // visit the same number of key tiles for every u, so all workgroups carry
@@ -184,6 +188,41 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
   auto init_bias = [&](const f32x4 (&bv)[4 * NH], f32x16 (&s)[NH], int i) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) s[h][i] = bv[4 * h + (i >> 2)][i & 3] * inv_scale;
+  };
+  // Tiles after the first go through the wave's own LDS rows: direct loads
+  // that cover whole bias rows (RPI rows of RB bytes per 1 KiB load: 8 or 4
+  // cache lines, not the 32 of a 16-byte read from each row), then one
+  // 16-byte read per 4 keys in the accumulator layout.  Row r keeps logical
+  // 16-byte chunk c at physical chunk c ^ bswz(r), so that the 16 rows of a
+  // read pass meet 16 different bank groups.  Each wave reads only the rows it
+  // loaded, and loads a tile only after reading the one before: no barrier.
+  // Rows past N load whatever the resource returns (zeros past the slice);
+  // they are never written.
+  constexpr int RB = BN * 4, RPI = 1024 / RB, LPR = RB / 16, NBL = BN / 8, NX = RB == 128 ? 2 : 4;
+  auto bswz = [](int r) __attribute__((always_inline)) { return RB == 128 ? (r >> 1) & 7 : r & 15; };
+  [[maybe_unused]] int* const lbw = lside + wave * 32 * BN;
+  // per-lane byte offsets of the loads, by x % NX (the swizzle of row RPI x +
+  // l / LPR depends on x only through x % NX); the row step RPI x is scalar
+  [[maybe_unused]] uint32_t bld[NX];
+  if constexpr (BIAS) {
+    const int ln = lane_id_here(), u = ln / LPR;
+#pragma unroll
+    for (int x = 0; x < NX; ++x)
+      bld[x] = (uint32_t)((long long)(q0 + u) * bias.sq * 4) + 16u * (uint32_t)((ln % LPR) ^ bswz(RPI * x + u));
+  }
+  auto stage_bias = [&](int key0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < NBL; ++x)
+      load_lds16(brs, lbw + 256 * x, bld[x % NX],
+                 (uint32_t)(RPI * x) * (uint32_t)bias.sq * 4u + (uint32_t)key0 * 4u);
+  };
+  auto read_bias = [&](f32x4 (&bv)[4 * NH]) __attribute__((always_inline)) {
+    const int ln = lane_id_here(), r = ln & 31;
+    const uint32_t z = (uint32_t)(wave * 32 * RB + r * RB + 16 * ((ln >> 5) ^ bswz(r)));
+#pragma unroll
+    for (int x = 0; x < 4 * NH; ++x)  // logical chunk 8 h + 2 j + g, x = 4 h + j
+      bv[x] = *reinterpret_cast<const f32x4*>(
+          reinterpret_cast<const char*>(lside) + (z ^ (uint32_t)(16 * (8 * (x >> 2) + 2 * (x & 3)))));
   };
 
 
@@ -362,15 +401,17 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     if constexpr (decltype(parity)::value == 0) return sa;
     else return sb;
   };
-  // Bias of tile t + 1: loaded at the start of step t - 1 (tiles 0 and 1
-  // here) and turned into the starting value of S_{t+1} at the end of that
-  // step, once P_{t-1} no longer needs the registers S_{t+1} will use.
+  // Bias of tile t + 1: staged at the start of step t - 1 (tile 1 here; tile
+  // 0 straight into registers) and turned into the starting value of S_{t+1}
+  // at the end of that step, once P_{t-1} no longer needs the registers
+  // S_{t+1} will use.
   [[maybe_unused]] f32x4 bv0[4 * NH], bv[4 * NH];
   if constexpr (BIAS) {
     load_bias(bv0, 0);
-    load_bias(bv, BN);
+    stage_bias(BN);
   }
   barrier_vm<0>();  // the block's Q rows, K_0 and V_0 (issue()) have landed
+  if constexpr (BIAS) read_bias(bv);
   {
     const int ln_r = lane_id_here();
 #pragma unroll
@@ -426,7 +467,7 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
     const float mneg = neg_ref();
     const int key1 = (j + 1) * BN;
     // tile j + 2's bias, ahead of this step's staging loads
-    if constexpr (BIAS) load_bias(bv, key1 + BN);
+    if constexpr (BIAS) stage_bias(key1 + BN);
     const auto kres = tile_rsrc(Kh, (j + 2) * BN);
     const auto vres = tile_rsrc(Vh, (j + 1) * BN);
     bf16x8 pk[2 * NH];
@@ -498,7 +539,8 @@ __global__ __launch_bounds__(64 * WAVES, D == 64 && !BIAS ? 3 : 8 / WAVES) void 
       }
       if constexpr (BIAS) {  // S_{j+2} starts from its bias, once P_j is packed
         constexpr int K0 = EXP_OPS + 2, NI = NOPS - K0;
-        static_assert(NI > 0, "no product left after the exp phases");
+        static_assert(NI > 0 && K0 >= 2, "no product left after the exp phases");
+        if (k == K0 - 2) read_bias(bv);
         if (k >= K0) {
 #pragma unroll
           for (int i = (k - K0) * 16 / NI; i < (k - K0 + 1) * 16 / NI; ++i) init_bias(bv, sc, i);
