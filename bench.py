@@ -179,14 +179,33 @@ def time_main(w, steps, warmup, warm_s=0.0):
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
 
-    for _ in range(warmup):
-        step(events())
-    if warm_s > 0:
-        warm_until(lambda: step(events()), warm_s)
-    torch.cuda.synchronize()
+    # Every event the timed steps use is created (recorded once) before the
+    # warm-up, and the warm-up reuses one set: nothing is allocated between
+    # the warm-up and the timed steps, so the GPU does not sit idle there.
+    # (After an idle gap of tens of ms the chip boosts its clock, overshoots
+    # its power limit and takes ~20 launches of this kernel to settle: steps
+    # timed in that window measure the power controller, not the kernel.)
     evs = [events() for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in [start, end] + [x for ev in evs for x in ev]:
+        e.record()
+    warm_ev = events()
+    for _ in range(warmup):
+        step(warm_ev)
+    n_warm, tw = 0, time.perf_counter()
+    if warm_s > 0:
+        n_warm = warm_until(lambda: step(warm_ev), warm_s)
     torch.cuda.synchronize()
+    step_s = (time.perf_counter() - tw) / n_warm if n_warm else 0.0
+    # A queue of about 40 ms of untimed steps ahead of the start event: the
+    # host then enqueues the timed steps while the GPU is still busy, so a
+    # stall of the host thread (seen on fresh machines: 30+ ms inside the
+    # loop, the GPU idle meanwhile and then ramping its clock back) cannot
+    # leave the GPU without work inside the timed region.  The timed region
+    # is still exactly `steps` steps between two events on the stream.
+    ahead = min(200, int(math.ceil(0.04 / step_s))) if step_s > 0 else 0
+    for _ in range(ahead):
+        step(warm_ev)
     t0 = time.perf_counter()
     start.record()
     for i in range(steps):
@@ -203,12 +222,15 @@ def time_calls(fn, reps, warmup, warm_s=0.0):
     """Mean and median of `reps` event-timed calls of fn after warm-up."""
     import torch
 
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:  # created before the warm-up (see time_main)
+        a.record()
+        b.record()
     for _ in range(warmup):
         fn()
     if warm_s > 0:
         warm_until(fn, warm_s)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
     torch.cuda.synchronize()
     for a, b in evs:
         a.record()
