@@ -6,8 +6,11 @@ input.  The default workload is the bf16 causal forward at B=2, H=32, N=8192,
 d=128 (one fa_fwd per step); with --workload a fwd+bwd workload steps through
 the forward and the backward stages (fa_bwd_dq, which also forms delta, then
 fa_bwd_dkdv -- exactly what fa_bwd enqueues for bf16).  Inputs are resident in
-device memory before the timed region starts.  Each kernel is bracketed by HIP
-events on the stream it runs on, so per-kernel durations are measured live.
+device memory before the timed region starts.  The timed steps run back to
+back between two HIP events on the stream the kernels run on (no event between
+kernels: recording one makes the next kernel start cold); a step of several
+kernels also times each kernel alone, `steps` launches between two events, so
+per-kernel durations are measured live.
 
 After the timed steps the other workloads are timed the same way and reported
 in the same JSON line: the bf16 causal forward+backward at B=2, H=16, N=4096,
@@ -166,35 +169,41 @@ def time_main(w, steps, warmup, warm_s=0.0):
     stages = ["fwd"] + (bwd_stages if w.backward else [])
     calls = {"delta": fa.fa_bwd_delta, "dkdv": fa.fa_bwd_dkdv, "dq": fa.fa_bwd_dq}
 
-    def step(ev):
-        ev[0].record()
-        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, descale=inp.descale)
-        ev[1].record()
-        if w.backward:
-            args = (q, k, v, o, do, lse, dq, dk, dv, ws, w.scale, w.causal)
-            for i, s in enumerate(stages[1:]):
-                calls[s](*args)
-                ev[i + 2].record()
+    args = (q, k, v, o, do, lse, dq, dk, dv, ws, w.scale, w.causal) if w.backward else None
 
-    def events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+    def run_stage(s):
+        if s == "fwd":
+            fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, descale=inp.descale)
+        else:
+            calls[s](*args)
 
-    # Every event the timed steps use is created (recorded once) before the
-    # warm-up, and the warm-up reuses one set: nothing is allocated between
-    # the warm-up and the timed steps, so the GPU does not sit idle there.
-    # (After an idle gap of tens of ms the chip boosts its clock, overshoots
-    # its power limit and takes ~20 launches of this kernel to settle: steps
-    # timed in that window measure the power controller, not the kernel.)
-    evs = [events() for _ in range(steps)]
+    def step():
+        for s in stages:
+            run_stage(s)
+
+    # The timed steps run back to back between two events, with no event in
+    # between: recording one between two kernels makes the next start cold
+    # (~45 us on the N=8192 forward), which would be timed as the step's.  A
+    # step of one kernel is therefore its average launch duration (gaps
+    # included).  A step of several kernels is timed the same way, and each
+    # kernel's average launch duration comes from `steps` launches of that
+    # kernel alone between two events right after (each stage only reads what
+    # the stages before it wrote, so repeating it changes nothing).
+    # Every event is created (recorded once) before the warm-up, so nothing is
+    # allocated between the warm-up and the timed steps and the GPU does not
+    # sit idle there.  (After an idle gap of tens of ms the chip boosts its
+    # clock, overshoots its power limit and takes ~20 launches of this kernel
+    # to settle: steps timed in that window measure the power controller.)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for e in [start, end] + [x for ev in evs for x in ev]:
+    sev = {s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for s in stages}
+    for e in [start, end] + [x for pair in sev.values() for x in pair]:
         e.record()
-    warm_ev = events()
     for _ in range(warmup):
-        step(warm_ev)
+        step()
     n_warm, tw = 0, time.perf_counter()
     if warm_s > 0:
-        n_warm = warm_until(lambda: step(warm_ev), warm_s)
+        n_warm = warm_until(step, warm_s)
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - tw) / n_warm if n_warm else 0.0
     # A queue of about 40 ms of untimed steps ahead of the start event: the
@@ -205,25 +214,41 @@ def time_main(w, steps, warmup, warm_s=0.0):
     # is still exactly `steps` steps between two events on the stream.
     ahead = min(200, int(math.ceil(0.04 / step_s))) if step_s > 0 else 0
     for _ in range(ahead):
-        step(warm_ev)
+        step()
     t0 = time.perf_counter()
     start.record()
-    for i in range(steps):
-        step(evs[i])
+    for _ in range(steps):
+        step()
     end.record()
+    if len(stages) > 1:
+        for s in stages:
+            a, b = sev[s]
+            a.record()
+            for _ in range(steps):
+                run_stage(s)
+            b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    per = {s: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i, s in enumerate(stages)}
+    if len(stages) == 1:
+        per = {stages[0]: total_ms / steps}
+    else:
+        per = {s: sev[s][0].elapsed_time(sev[s][1]) / steps for s in stages}
     return total_ms / steps, wall, per
 
 
-def time_calls(fn, reps, warmup, warm_s=0.0):
-    """Mean and median of `reps` event-timed calls of fn after warm-up."""
+def time_calls(fn, reps, warmup, warm_s=0.0, batches=5):
+    """Mean and median time per call of fn after warm-up: `batches` batches
+    of about reps/batches back-to-back calls, each batch between two events
+    (an event between every two calls would be timed too: recording one makes
+    the next kernel start cold, ~45 us on the N=8192 forward); the mean over
+    all calls and the median of the batch means."""
     import torch
 
+    batches = max(1, min(batches, reps))
+    per_batch = max(1, reps // batches)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
+           for _ in range(batches)]
     for a, b in evs:  # created before the warm-up (see time_main)
         a.record()
         b.record()
@@ -239,10 +264,11 @@ def time_calls(fn, reps, warmup, warm_s=0.0):
             fn()
     for a, b in evs:
         a.record()
-        fn()
+        for _ in range(per_batch):
+            fn()
         b.record()
     torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    ms = sorted(a.elapsed_time(b) / per_batch for a, b in evs)
     return sum(ms) / len(ms), ms[len(ms) // 2]
 
 
