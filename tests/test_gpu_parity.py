@@ -115,17 +115,28 @@ def test_full_bf16_causal_fwd_bwd_b2h16n4096d128():
     for name, t in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
         assert torch.isfinite(t.float()).all(), name
     for (b, h) in [(0, 0), (1, 15)]:
-        qs, ks, vs, dos = (exact_values(x[b, h], "bf16")
-                           for x in (inp.q, inp.k, inp.v, inp.dout))
+        qs = exact_values(inp.q[b, h], "bf16")
+        ks, vs = (exact_values(x[b, h], "bf16") for x in (inp.k, inp.v))
         o_ref, lse_ref = oracle.attn_fwd_rows(qs, ks, vs, rows, w.scale, w.causal)
         check(f"{w.name} ({b},{h}) O rows", to_f64(o[b, h])[rows], o_ref, "bf16")
         check(f"{w.name} ({b},{h}) LSE rows", to_f64(lse[b, h])[rows], lse_ref, "bf16", lse=True)
-        say(f"{w.name} ({b},{h}): oracle backward for the whole head")
-        rq, rk, rv = oracle.attn_bwd(qs[None, None], ks[None, None], vs[None, None],
-                                     dos[None, None], w.scale, w.causal)
-        check(f"{w.name} ({b},{h}) dQ", to_f64(dq[b, h]), rq[0, 0], "bf16")
-        check(f"{w.name} ({b},{h}) dK", to_f64(dk[b, h]), rk[0, 0], "bf16")
-        check(f"{w.name} ({b},{h}) dV", to_f64(dv[b, h]), rv[0, 0], "bf16")
+    # every (b, h), whole heads: forward and backward against the oracle (a
+    # wrong head or block order in any of the three kernels shows up here)
+    o64, lse64, dq64, dk64, dv64 = (to_f64(t) for t in (o, lse, dq, dk, dv))
+    for b in range(w.B):
+        for h in range(w.H):
+            qs, ks, vs, dos = (exact_values(x[b, h], "bf16")
+                               for x in (inp.q, inp.k, inp.v, inp.dout))
+            say(f"{w.name} ({b},{h}): oracle forward and backward for the whole head")
+            o_ref, lse_ref = oracle.attn_fwd(qs[None, None], ks[None, None], vs[None, None],
+                                             w.scale, w.causal)
+            check(f"{w.name} ({b},{h}) O", o64[b, h], o_ref[0, 0], "bf16")
+            check(f"{w.name} ({b},{h}) LSE", lse64[b, h], lse_ref[0, 0], "bf16", lse=True)
+            rq, rk, rv = oracle.attn_bwd(qs[None, None], ks[None, None], vs[None, None],
+                                         dos[None, None], w.scale, w.causal)
+            check(f"{w.name} ({b},{h}) dQ", dq64[b, h], rq[0, 0], "bf16")
+            check(f"{w.name} ({b},{h}) dK", dk64[b, h], rk[0, 0], "bf16")
+            check(f"{w.name} ({b},{h}) dV", dv64[b, h], rv[0, 0], "bf16")
 
 
 # --------------------------------------------------------------------------- #
