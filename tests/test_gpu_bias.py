@@ -279,3 +279,45 @@ def test_longest_sequence_keypad_bias(d, causal):
     dead = check_lse(f"{tag} LSE rows", lse64[0, 0, rows], lse_ref, "bf16")
     assert np.all(o64[0, 0, rows][dead] == 0.0)
     check(f"{tag} O rows", o64[0, 0, rows], o_ref, "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bias_rows_past_the_end_wrap(d, causal):
+    """A bias slice at the limit the library accepts: N = 1025 rows with a
+    row stride of 1048572 floats, so ((N-1) stride + N) floats fill 4 GiB
+    less a few KiB.  The last row block's 127 padding rows (1025..1151) then
+    sit past 2^32 bytes: the 32-bit offsets of their bias loads wrap (the
+    forward stages bias rows without clamping them, the backward's row offsets
+    are formed the same way) and read somewhere inside the slice.  Those rows
+    are never written; every real row must still match the oracle, forward
+    and backward."""
+    N = 1025
+    sq = ((2**32 - 4096 - 4 * N) // (4 * (N - 1))) // 4 * 4
+    assert (N - 1) * sq * 4 < 2**32 <= N * sq * 4
+    inp = fa_inputs.make_inputs((1, 2, N, d), "bf16", seed=17 * d + int(causal))
+    dense = fa_inputs.draw_bias((1, 1), N, seed=d, kind="dense")[0, 0, :, :N]
+    buf = torch.zeros((N - 1) * sq + N, dtype=torch.float32, device="cuda")
+    bias = torch.as_strided(buf, (1, 1, N, N), (0, 0, sq, 1))
+    bias[0, 0].copy_(torch.from_numpy(np.ascontiguousarray(dense)))
+    scale = 1 / math.sqrt(d)
+    dev = tuple(to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    tag = f"bias stride {sq} 1x2x{N}x{d} causal={causal}"
+    say(f"{tag}: fwd")
+    o, lse = run_fwd_bias(dev, bias, scale, causal, "bf16")
+    qs, ks, vs = (exact_values(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    bias_ref = dense.astype(np.float64)[None, None]
+    o_ref, lse_ref = oracle.attn_fwd(qs, ks, vs, scale, causal, bias=bias_ref)
+    dead = check_lse(f"{tag} LSE", to_f64(lse), lse_ref, "bf16")
+    assert np.all(to_f64(o)[dead] == 0.0)
+    check(f"{tag} O", to_f64(o), o_ref, "bf16")
+    say(f"{tag}: bwd")
+    dout = to_device(inp.dout, "bf16")
+    dq, dk, dv = run_bwd_bias(dev, bias, o, lse, dout, scale, causal)
+    rq, rk, rv = oracle.attn_bwd(qs, ks, vs, exact_values(inp.dout, "bf16"), scale, causal,
+                                 bias=bias_ref)
+    check(f"{tag} dQ", to_f64(dq), rq, "bf16")
+    check(f"{tag} dK", to_f64(dk), rk, "bf16")
+    check(f"{tag} dV", to_f64(dv), rv, "bf16")
+    del buf, bias
+    torch.cuda.empty_cache()
