@@ -624,6 +624,8 @@ def main():
                          "in device memory) on the two IO-comparison workloads")
     ap.add_argument("--hbm-calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--bias-only", action="store_true",
+                    help="only time the workloads with an additive bias (for profiling them)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: every (batch, head) is independent, so "
@@ -643,6 +645,14 @@ def main():
     if args.io_compare:
         print(json.dumps({"io_comparison": time_io_compare(max(3, args.steps), args.warmup)}),
               flush=True)
+        return
+
+    if args.bias_only:
+        out = {}
+        for name, shape, causal, kind, window, backward in BIAS_EXTRA:
+            out[name] = time_bias(shape, causal, kind, window, backward, max(3, args.steps),
+                                  args.warmup, args.warm_seconds)
+        print(json.dumps({"bias_workloads": out}), flush=True)
         return
 
     w = fa_inputs.WORKLOADS[args.workload]
